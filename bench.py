@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+One step = one pass of both halves of the hot path over resident synthetic
+inputs:
+  * attn_fwd on the causal GQA prefill workload (B=1, 12 query heads sharing
+    2 K/V heads, T=8192, d=128, bf16, scale 1/sqrt(128)), and
+  * attn_paged_decode on the paged-KV decode workload (64 sequences, one
+    query token each, 12/2 heads, d=128, bf16, 16-token blocks, lengths
+    uniform in [512, 8192], blocks placed by a seeded permutation).
+
+`value` is the prefill's attention-forward throughput in TFLOP/s
+(algorithmic flops 4*d*Hq*T(T+1)/2 over the average kernel time measured
+with HIP events on the launch stream); the decode's GB/s (algorithmic bytes
+over its average time) is reported beside it.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak; paged decode GB/s & % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def prefill_flops(cfg) -> float:
+    pairs = cfg.N * (cfg.N + 1) / 2 if cfg.causal else cfg.N * cfg.N
+    return 4.0 * cfg.d * cfg.B * cfg.Hq * pairs
+
+
+def prefill_bytes(cfg) -> float:
+    es = 2 if cfg.dtype == "bf16" else 4
+    q = cfg.B * cfg.Hq * cfg.N * cfg.d * es
+    kv = cfg.B * cfg.Hkv * cfg.N * cfg.d * es
+    return q + 2 * kv + q + cfg.B * cfg.Hq * cfg.N * 4
+
+
+def decode_bytes(p, cfg) -> float:
+    """K and V of every cached position read once per kv head, plus q, o,
+    lse, the used block-table entries and the lengths."""
+    ctx = p["ctx_lens"].numpy().astype(np.int64)
+    kv = int(ctx.sum()) * cfg.Hkv * cfg.d * 2 * 2
+    qo = 2 * cfg.S * cfg.Hq * cfg.d * 2
+    table = int(((ctx + cfg.block_size - 1) // cfg.block_size).sum()) * 4
+    return kv + qo + cfg.S * cfg.Hq * 4 + table + cfg.S * 4
+
+
+def decode_flops(p, cfg) -> float:
+    return 4.0 * cfg.Hq * cfg.d * float(p["ctx_lens"].numpy().astype(np.int64).sum())
+
+
+def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=5):
+    """The fp64 oracle, as it stands, on the prefill workload's host copy.
+
+    The whole workload fits in a few seconds of host time, so the sample is
+    the full forward pass, repeated until about `min_seconds` have elapsed.
+    """
+    from oracle import exact as OA
+    qn, kn, vn = (t.to("cpu").double().numpy() for t in (q, k, v))
+    times = []
+    while len(times) < max_reps and sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        OA.attention(qn, kn, vn, cfg.scale, cfg.causal, workers=workers)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.mean(times))
+    return {"value": round(prefill_flops(cfg) / dt / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": len(times),
+            "sample": f"the full {cfg.name} forward (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, "
+                      f"T={cfg.N}, d={cfg.d}, causal), float64 numpy oracle on the host copy"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_tiled_self_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
+    from exact_tiled_self_amd import _lib
+    from exact_tiled_self_amd.inputs import DENSE_CONFIGS, PAGED_CONFIG, dense_inputs, paged_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pcfg = DENSE_CONFIGS["gqa_causal_t8192"]
+    dcfg = PAGED_CONFIG
+    q, k, v = dense_inputs(pcfg)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(pcfg.B, pcfg.Hq, pcfg.N, dtype=torch.float32, device=dev)
+    p = paged_inputs(dcfg)
+    pd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in p.items()}
+    od = torch.empty_like(pd["q"])
+    lsed = torch.empty(dcfg.S, dcfg.Hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(attn_paged_decode_workspace_size(dcfg.S, dcfg.Hq, dcfg.d, p["max_blocks"], 16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        attn_fwd(qd, kd, vd, scale=pcfg.scale, causal=True, o=o, lse=lse, stream=stream)
+
+    def decode():
+        attn_paged_decode(pd["q"], pd["k_cache"], pd["v_cache"], pd["block_table"], pd["ctx_lens"],
+                          16, dcfg.scale, o=od, lse=lsed, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+
+    # decode with the 256 MB last-level cache flushed before every call
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    fl_ms = []
+    for _ in range(max(5, K // 5)):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        decode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fl_ms.append(e0.elapsed_time(e1))
+    del flush
+
+    # parity spot check on the benchmarked buffers (sampled rows / sequences)
+    from oracle import exact as OA
+    rows = np.array([0, 1, 4095, 8190, 8191])
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    errs = []
+    for h in (0, 5, 6, 11):
+        ro, rl = OA.attention_rows(qn, kn, vn, pcfg.scale, True, 0, h, rows)
+        errs.append(float(np.abs(o[0, h, torch.as_tensor(rows)].double().cpu().numpy() - ro).max()))
+    sub = np.array([0, 31, 63])
+    ro, rl = OA.paged_decode(p["q"][sub].double().numpy(), p["k_cache"].float().numpy(),
+                             p["v_cache"].float().numpy(), p["block_table"].numpy()[sub],
+                             p["ctx_lens"].numpy()[sub], 16, dcfg.scale)
+    derr = float(np.abs(od[torch.as_tensor(sub)].double().cpu().numpy() - ro).max())
+
+    pf = prefill_flops(pcfg)
+    pre_avg = float(np.mean(pre_ms))
+    tflops = pf / (pre_avg * 1e-3) / 1e12
+    db = decode_bytes(p, dcfg)
+    dec_avg = float(np.mean(dec_ms))
+    gbps = db / (dec_avg * 1e-3) / 1e9
+    fl_avg = float(np.mean(fl_ms))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa_causal_t8192 prefill + paged_decode_s64 decode",
+            "prefill": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "T": pcfg.N, "d": pcfg.d,
+                        "causal": True, "dtype": "bf16", "input": "0.5*N(0,1), seed 2"},
+            "decode": {"S": dcfg.S, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d, "block_size": 16,
+                       "ctx": "uniform [512, 8192], seed 4", "sum_ctx": int(p["ctx_lens"].sum()),
+                       "num_blocks": p["num_blocks"]},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel<128, causal>",
+                     "per_launch": {"flops": pf, "avg_us": round(pre_avg * 1e3, 2),
+                                    "min_us": round(min(pre_ms) * 1e3, 2)}},
+        "decode": {"value": round(gbps, 1), "unit": "GB/s", "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                   "avg_us": round(dec_avg * 1e3, 2), "min_us": round(min(dec_ms) * 1e3, 2),
+                   "bytes": db, "flops": decode_flops(p, dcfg),
+                   "flushed_avg_us": round(fl_avg * 1e3, 2),
+                   "flushed_GBps": round(db / (fl_avg * 1e-3) / 1e9, 1),
+                   "kernels": "decode_partial_kernel<128> + decode_combine_kernel<128>"},
+        "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,
+                   "tolerance": 2e-2},
+        "wall_s_timed": round(wall, 3),
+        "library": _lib.library_path(),
+    }
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        out["cpu_baseline"] = cpu_baseline(pcfg, q, k, v, workers)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

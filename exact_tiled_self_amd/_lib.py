@@ -1,0 +1,166 @@
+"""ctypes binding of libattn.so: the C ABI's entry points under the same
+names, taking torch tensors for device memory and the current torch stream.
+
+Argument marshalling only: shapes are read from the tensors, outputs are
+allocated with torch when not given, and every computation happens in the
+library's HIP kernels.  Tensors must already be contiguous CUDA (HIP)
+tensors of the right dtype; nothing is copied or converted here.  A missing
+library or a non-OK status raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+__all__ = ["AttnError", "attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+           "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
+           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_BF16"]
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_NO_DEVICE, ATTN_ERR_LAUNCH = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_DTYPE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from the library (or the library is missing)."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_LIBRARY", LIB_PATH)
+
+
+def raw_library():
+    """The loaded CDLL with argument and return types declared."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise AttnError(-1, f"{path} is not built (python -m exact_tiled_self_amd.build)")
+        lib = ctypes.CDLL(path)
+        lib.attn_fwd.restype = ci
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp]
+        lib.attn_paged_decode_workspace_size.restype = sz
+        lib.attn_paged_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci]
+        lib.attn_paged_decode.restype = ci
+        lib.attn_paged_decode.argtypes = [vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci,
+                                          cf, ci, vp, sz, vp]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [ci]
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_abi_version.restype = ci
+        lib.attn_abi_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return raw_library().attn_abi_version()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = raw_library()
+        raise AttnError(status, f"{lib.attn_status_string(status).decode()}: "
+                                f"{lib.attn_last_error().decode()}")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream))
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, *, o=None, lse=None, want_lse=True, stream=None):
+    """Dense attention forward: returns (o, lse) (lse is None if not wanted).
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; float32 or bfloat16.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ptrs = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+            _dev(lse, "lse") if lse is not None else None]
+    st = raw_library().attn_fwd(*ptrs, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                _DTYPE[q.dtype], _stream_ptr(q.device, stream))
+    _check(st)
+    return o, lse
+
+
+def attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size=16) -> int:
+    return int(raw_library().attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size))
+
+
+def attn_paged_decode(q, k_cache, v_cache, block_table, ctx_lens, block_size=16, scale=None, *,
+                      o=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """Paged single-token decode: returns (o, lse).
+
+    q: [S, Hq, d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d];
+    block_table: int32 [S, max_blocks]; ctx_lens: int32 [S].
+    """
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [S, Hq, d] and the caches [num_blocks, Hkv, block_size, d]")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise ValueError("block_table and ctx_lens must be int32")
+    if q.dtype not in _DTYPE or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype")
+    S, Hq, d = q.shape
+    num_blocks, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or bs != block_size or block_table.dim() != 2 or block_table.shape[0] != S \
+            or tuple(ctx_lens.shape) != (S,):
+        raise ValueError("inconsistent decode shapes")
+    max_blocks = block_table.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = raw_library().attn_paged_decode(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(ctx_lens, "ctx_lens"), int(block_size),
+        _dev(o, "o"), _dev(lse, "lse") if lse is not None else None, S, Hq, Hkv, d, max_blocks,
+        num_blocks, float(scale), _DTYPE[q.dtype], _dev(workspace, "workspace"), ws_bytes,
+        _stream_ptr(q.device, stream))
+    _check(st)
+    return o, lse

@@ -1,0 +1,194 @@
+// C ABI of libattn.so: argument validation, device check and dispatch.
+//
+// Order of checks: every argument check first (no HIP runtime call, so the
+// same errors come back on a machine without a GPU), then the device check,
+// then the launch.  On any error nothing is enqueued.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/attn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Architecture check, cached per device: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+attn_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(ATTN_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    const char* forced = getenv("ATTN_FORCE_ARCH");   // test hook: pretend another architecture
+    if (forced && *forced) {
+        if (strncmp(forced, "gfx950", 6) != 0)
+            return fail(ATTN_ERR_UNSUPPORTED, "device architecture %s is not gfx950", forced);
+        return ATTN_OK;
+    }
+    int st = dev < kMaxDevices ? g_arch[dev].load(std::memory_order_relaxed) : 0;
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ATTN_ERR_NO_DEVICE, "cannot query device %d", dev);
+        }
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (dev < kMaxDevices) g_arch[dev].store(st, std::memory_order_relaxed);
+        if (st == 2) return fail(ATTN_ERR_UNSUPPORTED, "device architecture %s is not gfx950", prop.gcnArchName);
+    }
+    if (st == 2) return fail(ATTN_ERR_UNSUPPORTED, "device architecture is not gfx950");
+    return ATTN_OK;
+}
+
+attn_status launch_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+}
+
+size_t elem_size(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_err; }
+
+const char* attn_status_string(attn_status s) {
+    switch (s) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_NO_DEVICE: return "ATTN_ERR_NO_DEVICE";
+        case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+    }
+    return "ATTN_STATUS_UNKNOWN";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                     int Hkv, int N, int d, float scale, int causal, attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "B, Hq, Hkv and N must be >= 1 (got %d, %d, %d, %d)", B, Hq, Hkv, N);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
+    if ((long long)N * d >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "N * d must be below 2^31");
+    const long long grid = (long long)B * Hq * ((N + 63) / 64);
+    if (grid >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t qbytes = (size_t)B * Hq * N * d * es, kvbytes = (size_t)B * Hkv * N * d * es;
+    const size_t lbytes = lse ? (size_t)B * Hq * N * 4 : 0;
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kvbytes) || overlap(o, qbytes, v, kvbytes) ||
+        overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kvbytes) ||
+        overlap(lse, lbytes, v, kvbytes) || overlap(lse, lbytes, o, qbytes))
+        return fail(ATTN_ERR_INVALID_ARG, "outputs must not overlap inputs or each other");
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+
+    attn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d;
+    a.c = (float)(fabs((double)scale) * 1.4426950408889634);
+    a.negate = scale < 0.f ? 1 : 0;
+    a.causal = causal;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launch_status(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s) : attn::launch_prefill_f32(a, s));
+}
+
+size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, int block_size) {
+    if (S < 1 || Hq < 1 || d < 1 || max_blocks < 1 || block_size != attn::kDecodeBlock) return 0;
+    const size_t nsplit = (size_t)attn::decode_num_splits(max_blocks);
+    return (size_t)S * Hq * nsplit * (size_t)(d + 2) * sizeof(float);
+}
+
+attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                              void* o, float* lse, int S, int Hq, int Hkv, int d, int max_blocks,
+                              int num_blocks, float scale, attn_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, ctx_lens and o must be non-null");
+    if (S < 1 || Hq < 1 || Hkv < 1 || max_blocks < 1 || num_blocks < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "S, Hq, Hkv, max_blocks and num_blocks must be >= 1");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports bf16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
+    if (block_size != attn::kDecodeBlock)
+        return fail(ATTN_ERR_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
+    if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
+    if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
+    if ((long long)num_blocks * Hkv * block_size * d >= (1LL << 40))
+        return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
+    if ((long long)S * Hkv * attn::decode_num_splits(max_blocks) >= (1LL << 31) || S > 65535 || Hkv > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "too many sequences or splits for one launch");
+    const size_t need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(workspace, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and workspace must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, ctx_lens and lse must be 4-byte aligned");
+    const size_t es = 2;
+    const size_t qb = (size_t)S * Hq * d * es, cb = (size_t)num_blocks * Hkv * block_size * d * es;
+    const size_t tb = (size_t)S * max_blocks * 4, lb = (size_t)S * 4, lsb = lse ? (size_t)S * Hq * 4 : 0;
+    const void* ins[5] = {q, k_cache, v_cache, block_table, ctx_lens};
+    const size_t insz[5] = {qb, cb, cb, tb, lb};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(o, qb, ins[i], insz[i]) || overlap(lse, lsb, ins[i], insz[i]) ||
+            overlap(workspace, need, ins[i], insz[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "outputs and workspace must not overlap the inputs");
+    if (overlap(o, qb, lse, lsb) || overlap(o, qb, workspace, need) || overlap(lse, lsb, workspace, need))
+        return fail(ATTN_ERR_INVALID_ARG, "o, lse and workspace must not overlap");
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+
+    attn::DecodeArgs a;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table; a.ctx_lens = ctx_lens;
+    a.o = o; a.lse = lse; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.max_blocks = max_blocks; a.num_blocks = num_blocks;
+    a.c = (float)(fabs((double)scale) * 1.4426950408889634);
+    a.negate = scale < 0.f ? 1 : 0;
+    a.workspace = static_cast<float*>(workspace);
+    return launch_status(attn::launch_paged_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Device-side helpers shared by the attention kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Flip the sign of the 8 bf16 lanes held in a 16-byte word (exact).
+__device__ __forceinline__ u32x4 neg_bf16x8(u32x4 v) {
+    const uint32_t s = 0x80008000u;
+    return u32x4{v.x ^ s, v.y ^ s, v.z ^ s, v.w ^ s};
+}
+
+// Pack two fp32 into two bf16 (round to nearest even) in one 32-bit word,
+// `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Wave-wide exchange with lane ^ mask (ds_bpermute based).
+__device__ __forceinline__ float xor_shfl(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+// Hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) {
+    return __builtin_amdgcn_exp2f(x);
+}
+
+}  // namespace attn

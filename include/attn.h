@@ -1,0 +1,149 @@
+/*
+ * attn.h - exact tiled scaled-dot-product attention forward on MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Every tensor argument is a plain pointer to DEVICE
+ * memory owned by the caller; sizes are plain integers; `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream).
+ *
+ * What is computed.  For each query row q_i and the keys k_j / values v_j it
+ * may attend to ("Autoatención, kernels CUDA y FlashAttention", section 1):
+ *
+ *     o_i   = sum_j softmax_j(scale * <q_i, k_j>) v_j
+ *     lse_i = ln sum_j exp(scale * <q_i, k_j>)          (natural log)
+ *
+ * The library evaluates this exactly (up to floating-point order) block by
+ * block with the online-softmax recurrence ("FlashAttention" notes, section
+ * "No basta con promediar los resultados de los bloques"): a running maximum
+ * m, sum l and numerator u per row, earlier l and u rescaled by e^(m - m')
+ * when a block raises the maximum, output u / l.  The N x N score matrix is
+ * never written to device memory (same page, introduction; first page,
+ * section 3).  Only o and the per-row statistic lse leave the chip; lse is
+ * the normalisation statistic kept for a backward pass (first page,
+ * section 3, "Recálculo durante la retropropagación").
+ *
+ * Ownership and concurrency.  The caller allocates and frees every buffer,
+ * including the decode workspace.  The library allocates no device memory,
+ * never synchronises, and never changes the current device: all work is
+ * enqueued on `stream` for the current device and runs asynchronously, so
+ * buffers must stay alive until that work completes.  Outputs are fully
+ * overwritten; inputs are only read and must not overlap the outputs.  The
+ * library keeps no state between calls apart from a per-device cache of the
+ * architecture check and a per-thread error string, so concurrent calls
+ * from several host threads are safe when their buffers are disjoint.
+ *
+ * Errors.  Every condition the host can check is checked synchronously,
+ * before anything is enqueued: on a non-OK return nothing has been launched
+ * and the outputs are untouched; attn_last_error() then gives a one-line
+ * reason.  There is no fallback path: unsupported shapes, dtypes or devices
+ * are errors.  Argument checks come before any HIP runtime call, so they
+ * behave the same with no GPU present.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, overlap,
+                                   Hq % Hkv != 0, non-finite scale, small workspace */
+    ATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented: head dim, dtype,
+                                   block size, group size, device architecture */
+    ATTN_ERR_NO_DEVICE = 3,     /* no HIP device is current / visible */
+    ATTN_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,               /* IEEE binary32 in and out, fp32 arithmetic throughout */
+    ATTN_BF16 = 1               /* bfloat16 in and out, fp32 accumulation */
+} attn_dtype;
+
+/*
+ * attn_fwd - dense attention forward (prefill), optionally causal, with
+ * grouped K/V heads.
+ *
+ *   q, o : [B, Hq,  N, d]  contiguous, element type `dtype`
+ *   k, v : [B, Hkv, N, d]  contiguous, element type `dtype`
+ *   lse  : [B, Hq,  N]     fp32, or NULL to skip it
+ *
+ * Query head h reads K/V head h / (Hq / Hkv) (contiguous groups; grouped-
+ * query attention, "FlashAttention" notes, last section).  With causal = 1,
+ * query row i attends to keys j <= i (diagonal included); with causal = 0
+ * to all N keys.  `scale` multiplies the dot products before the softmax
+ * (1/sqrt(d) in the pages' formula); any finite value is accepted.
+ * o is written in `dtype` (round-to-nearest-even for bf16).
+ *
+ * Supported: dtype F32 or BF16; d = 64 or 128; B, Hq, Hkv, N >= 1;
+ * N * d < 2^31; q, k, v, o 16-byte aligned; lse 4-byte aligned.
+ * Returns INVALID_ARG / UNSUPPORTED / NO_DEVICE / LAUNCH as described above.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     attn_dtype dtype, void* stream);
+
+/*
+ * attn_paged_decode_workspace_size - bytes of device workspace that
+ * attn_paged_decode needs for these sizes (0 on invalid sizes).  The
+ * workspace holds the fp32 partial states (m, l, u) of the key splits.
+ */
+size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, int block_size);
+
+/*
+ * attn_paged_decode - one new query token per sequence against a paged KV
+ * cache ("Kernels de atención rápida y fusión de operadores", section
+ * "Atención tipo FlashAttention y atención paginada"): the cache is a pool
+ * of fixed-size blocks and a block table maps each sequence's logical
+ * positions to physical blocks.
+ *
+ *   q, o          : [S, Hq, d]                          element type `dtype`
+ *   k_cache,
+ *   v_cache       : [num_blocks, Hkv, block_size, d]   element type `dtype`
+ *   block_table   : int32 [S, max_blocks]; logical position p of sequence s
+ *                   lives in block block_table[s][p / block_size], slot
+ *                   p % block_size.  Entries at or past
+ *                   ceil(ctx_lens[s] / block_size) are never read.
+ *   ctx_lens      : int32 [S]; the query attends to positions 0..ctx_lens[s]-1
+ *                   (its own K/V already appended).  0 gives o = 0, lse = -inf.
+ *   lse           : fp32 [S, Hq], or NULL
+ *   workspace     : device scratch of at least
+ *                   attn_paged_decode_workspace_size(S, Hq, d, max_blocks,
+ *                   block_size) bytes, 16-byte aligned; contents on entry
+ *                   are ignored.  Calls that share a workspace must be
+ *                   ordered on one stream.
+ *
+ * Supported: dtype BF16; d = 64 or 128; block_size = 16; Hq % Hkv == 0
+ * with Hq / Hkv <= 16; S, max_blocks, num_blocks >= 1.
+ *
+ * Device-resident values cannot be checked before launch.  A ctx_lens entry
+ * outside [0, max_blocks * block_size] or a needed block_table entry outside
+ * [0, num_blocks) never causes an out-of-bounds access: that sequence's
+ * outputs are set to NaN instead.
+ */
+attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              int block_size, void* o, float* lse, int S, int Hq, int Hkv,
+                              int d, int max_blocks, int num_blocks, float scale,
+                              attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Static string naming a status code. */
+const char* attn_status_string(attn_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects every host-checkable bad argument before touching the
+HIP runtime (so these run without a GPU).  No kernel is launched here: each
+call below fails validation, except the no-device check, which only runs
+where no GPU is present."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from exact_tiled_self_amd import _lib
+from exact_tiled_self_amd.build import LIB_PATH, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED, NO_DEVICE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+A = 0x100000          # fake, 16-byte aligned addresses: never dereferenced
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return _lib.raw_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert names == sorted(["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+                            "attn_status_string", "attn_last_error", "attn_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.attn_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED",
+                                 "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH"]):
+        assert lib.attn_status_string(code).decode() == name
+
+
+def fwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, Hq=4,
+        Hkv=2, N=128, d=128, scale=0.125, causal=0, dtype=BF16):
+    return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID), (dict(N=0), INVALID),
+    (dict(N=-5), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=math.inf), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(q=A + 8), INVALID), (dict(o=A + 192 * MB + 4), INVALID), (dict(lse=A + 256 * MB + 2), INVALID),
+    (dict(o=A), INVALID), (dict(lse=A + 64 * MB + 4096), INVALID), (dict(lse=A + 192 * MB), INVALID),
+    (dict(N=1 << 24, d=128), UNSUPPORTED),
+])
+def test_fwd_rejects_before_any_launch(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def dec(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A + 200 * MB, bs=16,
+        o=A + 208 * MB, lse=A + 216 * MB, S=4, Hq=12, Hkv=2, d=128, max_blocks=8, num_blocks=32,
+        scale=0.088, dtype=BF16, ws=A + 256 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_paged_decode_workspace_size(S, Hq, d, max_blocks, bs)
+    return lib.attn_paged_decode(q, kc, vc, table, ctx, bs, o, lse, S, Hq, Hkv, d, max_blocks,
+                                 num_blocks, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(kc=0), INVALID), (dict(table=0), INVALID), (dict(ctx=0), INVALID),
+    (dict(o=0), INVALID), (dict(S=0), INVALID), (dict(max_blocks=0), INVALID),
+    (dict(num_blocks=0), INVALID), (dict(Hq=12, Hkv=5), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(dtype=F32), UNSUPPORTED), (dict(d=80), UNSUPPORTED), (dict(bs=32), UNSUPPORTED),
+    (dict(Hq=34, Hkv=2), UNSUPPORTED), (dict(ws=0), INVALID), (dict(ws_bytes=16), INVALID),
+    (dict(q=A + 4), INVALID), (dict(table=A + 192 * MB + 2), INVALID), (dict(ws=A + 256 * MB + 8), INVALID),
+    (dict(o=A + 64 * MB), INVALID), (dict(ws=A + 200 * MB), INVALID),
+])
+def test_decode_rejects_before_any_launch(lib, kw, status):
+    assert dec(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_workspace_size(lib):
+    # fp32 partial state (m, l, u[d]) per query head and 256-token split
+    assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == 64 * 12 * 32 * 130 * 4
+    assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 16) == 1 * 1 * 1 * 66 * 4
+    assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 32) == 0
+    assert lib.attn_paged_decode_workspace_size(0, 1, 64, 1, 16) == 0
+
+
+def _gpu_present():
+    return os.path.exists("/dev/kfd") or torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid arguments would launch on a GPU")
+def test_no_device_status(lib):
+    assert fwd(lib) == NO_DEVICE
+    assert dec(lib) == NO_DEVICE
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        _lib.attn_fwd(q, q[:, :1], q[:, :1])
+    with pytest.raises(ValueError):
+        _lib.attn_fwd(q.to(torch.float16), q[:, :1], q[:, :1])

@@ -1,0 +1,155 @@
+"""GPU parity of attn_paged_decode against the float64 oracle: the full
+64-sequence workload, ragged lengths, NaN poison in every slot that must not
+be read, a spike key located through the block table, an identity table
+against dense attention, empty contexts and determinism."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_tiled_self_amd import attn_fwd, attn_paged_decode
+from exact_tiled_self_amd.inputs import PAGED_CONFIG, PagedConfig, paged_inputs
+from oracle import exact as OA
+from tests.gpu_util import DEV, LSE_TOL, O_TOL, announce, f64, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name_case(request):
+    announce(request.node.nodeid)
+    yield
+
+
+def _dev(p):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+
+
+def run_decode(p, scale, **kw):
+    d = _dev(p)
+    o, lse = attn_paged_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                               d["ctx_lens"], d["block_size"], scale, **kw)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def oracle_decode(p, scale):
+    return OA.paged_decode(f64(p["q"]), f64(p["k_cache"]), f64(p["v_cache"]),
+                           p["block_table"].numpy(), p["ctx_lens"].numpy(), p["block_size"], scale)
+
+
+def check(p, scale, name):
+    announce(f"decode {name} S={p['q'].shape[0]} nb={p['num_blocks']}")
+    o, lse = run_decode(p, scale)
+    ro, rl = oracle_decode(p, scale)
+    ctx = p["ctx_lens"].numpy()
+    live = ctx > 0
+    assert torch.isfinite(o.float()).all(), name
+    eo = max_abs(f64(o)[live], ro[live])
+    el = max_abs(lse.double().numpy()[live], rl[live])
+    assert eo <= O_TOL[torch.bfloat16], f"{name}: o max-abs {eo}"
+    assert el <= LSE_TOL, f"{name}: lse max-abs {el}"
+    if (~live).any():
+        assert torch.all(o[torch.from_numpy(~live)] == 0)
+        assert torch.all(torch.isneginf(lse[torch.from_numpy(~live)]))
+    return eo, el
+
+
+def small_cfg(Hq=12, Hkv=2, d=128):
+    return PagedConfig("small", S=1, Hq=Hq, Hkv=Hkv, d=d, block_size=16, ctx_lo=1, ctx_hi=1,
+                       max_blocks=1, dtype="bf16", seed=0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(12, 2), (8, 8), (16, 1), (6, 3)])
+def test_ragged_lengths_with_poison(d, Hq, Hkv):
+    ctx = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 700, 1024, 2000]
+    p = paged_inputs(small_cfg(Hq, Hkv, d), S=len(ctx), ctx_lens=ctx, poison=True,
+                     extra_blocks=5, max_blocks=130, seed=d + Hq)
+    check(p, 1.0 / math.sqrt(d), f"ragged d{d} {Hq}/{Hkv}")
+
+
+def test_empty_contexts():
+    ctx = [0, 5, 0, 300, 0]
+    p = paged_inputs(small_cfg(), S=5, ctx_lens=ctx, poison=True, extra_blocks=2, max_blocks=20, seed=3)
+    check(p, 0.0884, "empty")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.7])
+def test_unusual_scales(scale):
+    p = paged_inputs(small_cfg(), S=4, ctx_lens=[3, 40, 290, 513], poison=True, max_blocks=40, seed=9)
+    check(p, scale, f"scale={scale}")
+
+
+def test_spike_through_block_table():
+    """One key per sequence scores far above the rest at a random logical
+    position p*; the output must be the value at the physical slot that the
+    table maps p* to."""
+    cfg = small_cfg(Hq=12, Hkv=2, d=128)
+    ctx = [17, 100, 513, 1500, 4000, 8192]
+    rng = np.random.default_rng(17)
+    for rep in range(3):
+        p = paged_inputs(cfg, S=len(ctx), ctx_lens=ctx, poison=True, extra_blocks=3,
+                         max_blocks=512, seed=100 + rep)
+        q = torch.zeros_like(p["q"], dtype=torch.float32)
+        q[..., 0] = 1.0
+        kc = p["k_cache"].float()
+        kc[..., 0] = torch.where(torch.isnan(kc[..., 0]), kc[..., 0],
+                                 torch.from_numpy(rng.uniform(-1, 1, kc.shape[:-1]).astype(np.float32)))
+        t = p["block_table"].numpy()
+        targets = []
+        for s, n in enumerate(ctx):
+            ps = int(rng.integers(0, n))
+            blk, slot = int(t[s, ps // 16]), ps % 16
+            kc[blk, :, slot, 0] = 40.0
+            targets.append(p["v_cache"][blk, :, slot].double())
+        p["q"] = q.to(torch.bfloat16)
+        p["k_cache"] = kc.to(torch.bfloat16)
+        o, _ = run_decode(p, 1.0)
+        for s in range(len(ctx)):
+            for h in range(12):
+                g = h // 6
+                err = (o[s, h].double() - targets[s][g]).abs().max().item()
+                assert err <= 1e-2, (rep, s, h, err)
+
+
+def test_identity_table_matches_dense():
+    """A contiguous cache with an identity table is ordinary single-query
+    attention: compare with the dense kernel on the same keys."""
+    S, Hq, Hkv, d, n = 3, 12, 2, 128, 1000
+    nb = (n + 15) // 16
+    gen = torch.Generator().manual_seed(5)
+    K = torch.randn(S, Hkv, nb * 16, d, generator=gen).to(torch.bfloat16)
+    V = torch.randn(S, Hkv, nb * 16, d, generator=gen).to(torch.bfloat16)
+    q = torch.randn(S, Hq, d, generator=gen).to(torch.bfloat16)
+    kc = K.view(S, Hkv, nb, 16, d).permute(0, 2, 1, 3, 4).reshape(S * nb, Hkv, 16, d).contiguous()
+    vc = V.view(S, Hkv, nb, 16, d).permute(0, 2, 1, 3, 4).reshape(S * nb, Hkv, 16, d).contiguous()
+    table = torch.arange(S * nb, dtype=torch.int32).view(S, nb)
+    ctx = torch.full((S,), n, dtype=torch.int32)
+    p = dict(q=q, k_cache=kc, v_cache=vc, block_table=table, ctx_lens=ctx, block_size=16,
+             num_blocks=S * nb, max_blocks=nb)
+    o, lse = run_decode(p, 0.0884)
+    for s in range(S):
+        # dense kernel: the decode query as row n-1 of a causal prefill over n keys
+        qd = torch.zeros(1, Hq, n, d, dtype=torch.bfloat16)
+        qd[0, :, n - 1] = q[s]
+        od, ld = attn_fwd(qd.to(DEV), K[s:s + 1, :, :n].contiguous().to(DEV),
+                          V[s:s + 1, :, :n].contiguous().to(DEV), scale=0.0884, causal=True)
+        torch.cuda.synchronize()
+        assert max_abs(f64(o[s]), f64(od[0, :, n - 1])) <= 1e-2
+        assert max_abs(lse[s].double().numpy(), ld[0, :, n - 1].double().cpu().numpy()) <= 1e-4
+
+
+def test_full_workload_with_poison():
+    p = paged_inputs(PAGED_CONFIG, poison=True, extra_blocks=64)
+    check(p, PAGED_CONFIG.scale, "paged_decode_s64 poison")
+
+
+def test_full_workload_and_determinism():
+    p = paged_inputs(PAGED_CONFIG)
+    eo, el = check(p, PAGED_CONFIG.scale, "paged_decode_s64")
+    o1, l1 = run_decode(p, PAGED_CONFIG.scale)
+    o2, l2 = run_decode(p, PAGED_CONFIG.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

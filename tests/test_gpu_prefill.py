@@ -1,0 +1,310 @@
+"""GPU parity of attn_fwd against the float64 oracle (element by element at
+small sizes, sampled rows at the full workload sizes), plus the probes whose
+answer is fixed in closed form, exact selection of masked / grouped
+positions, guard regions, determinism and host-forced error paths."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from exact_tiled_self_amd import AttnError, attn_fwd
+from exact_tiled_self_amd.inputs import DENSE_CONFIGS, dense_inputs
+from oracle import exact as OA
+from tests.gpu_util import (DEV, LSE_TOL, O_TOL, announce, check_dense_full, check_dense_rows,
+                            f64, max_abs, run_fwd)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(autouse=True)
+def _name_case(request):
+    announce(request.node.nodeid)
+    yield
+
+
+# ------------------------------------------------------------ sweeps ----
+
+SWEEP_N = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 196, 577]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SWEEP_N)
+def test_sweep_sizes(dtype, d, causal, N):
+    q, k, v = dense_inputs(B=1, Hq=2, Hkv=1, N=N, d=d, dtype=dtype, seed=1000 + N)
+    check_dense_full(q, k, v, 1.0 / math.sqrt(d), causal, f"N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [
+    (2, 6, 2, 300, 128, True), (2, 6, 3, 260, 64, False), (3, 4, 4, 129, 64, True),
+    (1, 8, 1, 520, 128, False), (1, 12, 2, 700, 128, True),
+])
+def test_gqa_batches(dtype, B, Hq, Hkv, N, d, causal):
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=7 * N + Hq)
+    check_dense_full(q, k, v, 1.0 / math.sqrt(d), causal, f"B{B}H{Hq}/{Hkv}N{N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_unusual_scales(dtype, scale):
+    q, k, v = dense_inputs(B=1, Hq=2, Hkv=2, N=150, d=64, dtype=dtype, seed=31)
+    for causal in (False, True):
+        check_dense_full(q, k, v, scale, causal, f"scale={scale}")
+
+
+# ------------------------------------------------- the pages' example ----
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_worked_example(dtype, d):
+    """Scores 0, 0, ln3, ln3 with values 0, 0, 1, 1 give 0.75 (not the 0.5 of
+    averaging two blocks).  In bf16 every input is exact: k in {0, 1} and the
+    scale is float32(ln 3)."""
+    dt = DT[dtype]
+    q = torch.zeros(1, 1, 4, d); q[..., 0] = 1.0
+    k = torch.zeros(1, 1, 4, d); k[0, 0, :, 0] = torch.tensor([0.0, 0.0, 1.0, 1.0])
+    v = torch.zeros(1, 1, 4, d); v[0, 0, :, 0] = torch.tensor([0.0, 0.0, 1.0, 1.0])
+    o, lse = run_fwd(q.to(dt), k.to(dt), v.to(dt), math.log(3.0), False)
+    o = o.double()
+    if dt == torch.bfloat16:
+        assert torch.all(o[0, 0, :, 0] == 0.75)
+    else:
+        assert torch.all((o[0, 0, :, 0] - 0.75).abs() <= 1e-7)
+    assert torch.all(o[0, 0, :, 1:] == 0.0)
+    assert torch.all((lse[0, 0].double() - math.log(2 + 2 * math.exp(float(np.float32(math.log(3.0)))))).abs() < 1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_worked_example_across_tiles(dtype, reverse):
+    """The same two pairs of keys placed in different key tiles (positions 0,1
+    and 64,65), every other key with score about -30000 (weight exactly 0):
+    the rescale between tiles must still give 0.75."""
+    dt = DT[dtype]
+    N, d = 256, 128
+    gen = torch.Generator().manual_seed(5)
+    q = torch.zeros(1, 1, N, d); q[..., 0] = 1.0
+    k = torch.zeros(1, 1, N, d); k[0, 0, :, 0] = -27307.0
+    v = torch.randn(1, 1, N, d, generator=gen)
+    lo, hi = ((64, 65), (0, 1)) if reverse else ((0, 1), (64, 65))
+    for j in lo:
+        k[0, 0, j, 0] = 0.0; v[0, 0, j, 0] = 0.0
+    for j in hi:
+        k[0, 0, j, 0] = 1.0; v[0, 0, j, 0] = 1.0
+    o, _ = run_fwd(q.to(dt), k.to(dt), v.to(dt), math.log(3.0), False)
+    col = o[0, 0, :, 0].double()
+    assert torch.all((col - 0.75).abs() <= (0.0 if dt == torch.bfloat16 else 1e-7))
+
+
+# ------------------------------------------------------ closed forms ----
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_uniform_scores(dtype, causal):
+    """scale 0: o_i is the mean of the allowed values (a prefix mean when
+    causal) and lse_i = ln(#allowed)."""
+    N, d = 200, 64
+    q, k, v = dense_inputs(B=1, Hq=2, Hkv=1, N=N, d=d, dtype=dtype, seed=3)
+    o, lse = run_fwd(q, k, v, 0.0, causal)
+    vv = f64(v)[0, 0]
+    if causal:
+        expect = np.cumsum(vv, axis=0) / np.arange(1, N + 1)[:, None]
+        el = np.log(np.arange(1, N + 1))
+    else:
+        expect = np.broadcast_to(vv.mean(axis=0), (N, d))
+        el = np.full(N, math.log(N))
+    for h in range(2):
+        assert max_abs(f64(o)[0, h], expect) <= O_TOL[DT[dtype]]
+        assert max_abs(lse[0, h].double().numpy(), el) <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_constant_values(dtype):
+    """Constant V gives exactly that constant, whatever the scores."""
+    N, d = 333, 128
+    q, k, _ = dense_inputs(B=1, Hq=2, Hkv=1, N=N, d=d, dtype=dtype, seed=4, amp=3.0)
+    c = torch.linspace(-2.0, 2.0, d).to(DT[dtype])
+    v = c.expand(1, 1, N, d).contiguous()
+    for causal in (False, True):
+        o, _ = run_fwd(q, k, v, 0.3, causal)
+        err = (o.double() - c.double()).abs().max().item()
+        assert err <= (0.0 if dtype == "bf16" else 1e-6), err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_values(dtype, d, causal):
+    """V = I (N = d) turns o into the probability matrix: rows sum to 1, it
+    matches the oracle, and the causal upper triangle is exactly zero."""
+    N = d
+    q, k, _ = dense_inputs(B=1, Hq=1, Hkv=1, N=N, d=d, dtype=dtype, seed=8)
+    v = torch.eye(N).reshape(1, 1, N, N).to(DT[dtype])
+    o, _ = run_fwd(q, k, v, 1.0 / math.sqrt(d), causal)
+    P = f64(o)[0, 0]
+    ro, _ = OA.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(d), causal)
+    assert max_abs(P, ro[0, 0]) <= O_TOL[DT[dtype]]
+    assert np.allclose(P.sum(axis=1), 1.0, atol=O_TOL[DT[dtype]] * 4)
+    if causal:
+        assert np.all(P[np.triu_indices(N, 1)] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_future_spike_is_masked(dtype):
+    """Causal: each row's largest score sits at the masked key j = i + 1; a
+    leak through the mask would move o by O(1)."""
+    N, d = 256, 64
+    c = 4.0
+    q = torch.zeros(1, 1, N, d)
+    k = torch.zeros(1, 1, N, d)
+    for i in range(N):
+        q[0, 0, i, (i + 1) % d] = c
+        k[0, 0, i, i % d] = c
+    v = torch.randn(1, 1, N, d, generator=torch.Generator().manual_seed(11))
+    dt = DT[dtype]
+    check_dense_full(q.to(dt), k.to(dt), v.to(dt), 1.0, True, "future-spike")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gqa_head_mapping(dtype):
+    """V of kv head g is the constant g + 1: query head h must give exactly
+    h // (Hq / Hkv) + 1.  Also GQA equals MHA with repeated K/V, bit for bit."""
+    B, Hq, Hkv, N, d = 2, 12, 3, 150, 128
+    q, k, _ = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=21)
+    v = torch.empty(B, Hkv, N, d)
+    for g in range(Hkv):
+        v[:, g] = g + 1.0
+    v = v.to(DT[dtype])
+    for causal in (False, True):
+        o, _ = run_fwd(q, k, v, 0.088, causal)
+        for h in range(Hq):
+            assert torch.all(o[:, h].double() == float(h // (Hq // Hkv) + 1))
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=22)
+    G = Hq // Hkv
+    o1, l1 = run_fwd(q, k, v, 0.088, True)
+    o2, l2 = run_fwd(q, k.repeat_interleave(G, 1), v.repeat_interleave(G, 1), 0.088, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------- guards & determinism ----
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_guard_regions(dtype, causal):
+    """Inputs sit inside NaN-filled buffers and outputs inside canary-filled
+    buffers: no read may leave the inputs, no write may leave the outputs."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 197, 128
+    dt = DT[dtype]
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=41)
+    pad = 4096
+
+    def guarded(t, fill):
+        buf = torch.full((t.numel() + 2 * pad,), fill, dtype=t.dtype, device=DEV)
+        view = buf[pad:pad + t.numel()].view(t.shape)
+        view.copy_(t.to(DEV))
+        return buf, view
+
+    _, qd = guarded(q, float("nan"))
+    _, kd = guarded(k, float("nan"))
+    _, vd = guarded(v, float("nan"))
+    obuf, od = guarded(torch.zeros_like(q), 1234.0)
+    lbuf = torch.full((B * Hq * N + 2 * pad,), -77.0, dtype=torch.float32, device=DEV)
+    ld = lbuf[pad:pad + B * Hq * N].view(B, Hq, N)
+    attn_fwd(qd, kd, vd, scale=1.0 / math.sqrt(d), causal=causal, o=od, lse=ld)
+    torch.cuda.synchronize()
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(d), causal)
+    assert max_abs(f64(od), ro) <= O_TOL[dt]
+    assert max_abs(ld.cpu().double().numpy(), rl) <= LSE_TOL
+    ob = obuf.cpu()
+    assert torch.all(ob[:pad] == 1234.0) and torch.all(ob[-pad:] == 1234.0)
+    lb = lbuf.cpu()
+    assert torch.all(lb[:pad] == -77.0) and torch.all(lb[-pad:] == -77.0)
+
+
+def test_no_lse_output():
+    q, k, v = dense_inputs(B=1, Hq=2, Hkv=1, N=100, d=64, dtype="bf16", seed=2)
+    o1, _ = run_fwd(q, k, v, 0.125, True, want_lse=False)
+    o2, _ = run_fwd(q, k, v, 0.125, True)
+    assert torch.equal(o1, o2)
+
+
+def test_determinism():
+    cfg = DENSE_CONFIGS["gqa_causal_t8192"]
+    q, k, v = (t.to(DEV) for t in dense_inputs(cfg))
+    outs = []
+    for _ in range(3):
+        o, lse = attn_fwd(q, k, v, scale=cfg.scale, causal=True)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+def test_forced_foreign_arch_is_rejected(monkeypatch):
+    """The architecture check, forced from the host: nothing is launched and
+    the output keeps its contents."""
+    q, k, v = (t.to(DEV) for t in dense_inputs(B=1, Hq=2, Hkv=1, N=64, d=64, dtype="bf16"))
+    o = torch.full_like(q, 5.0)
+    monkeypatch.setenv("ATTN_FORCE_ARCH", "gfx942")
+    with pytest.raises(AttnError) as ei:
+        attn_fwd(q, k, v, o=o, causal=False)
+    assert ei.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(o == 5.0)
+
+
+# ------------------------------------------------- workload configs ----
+
+def test_config_vit_fp32_full():
+    cfg = DENSE_CONFIGS["vit_b16_fp32"]
+    check_dense_full(*dense_inputs(cfg), cfg.scale, cfg.causal, cfg.name)
+
+
+def test_config_vit_bf16_batched():
+    cfg = DENSE_CONFIGS["vit_b16_bf16"]
+    q, k, v = dense_inputs(cfg)
+    announce(cfg.name)
+    o, lse = run_fwd(q, k, v, cfg.scale, cfg.causal)
+    for b in (0, 17, 63):
+        ro, rl = OA.attention(f64(q[b:b + 1]), f64(k[b:b + 1]), f64(v[b:b + 1]), cfg.scale, False)
+        assert max_abs(f64(o[b:b + 1]), ro) <= O_TOL[q.dtype]
+        assert max_abs(lse[b:b + 1].double().numpy(), rl) <= LSE_TOL
+
+
+def test_config_vit_bf16_n577():
+    cfg = DENSE_CONFIGS["vit_b16_bf16_n577"]
+    q, k, v = dense_inputs(cfg)
+    announce(cfg.name)
+    o, lse = run_fwd(q, k, v, cfg.scale, cfg.causal)
+    for b in (0, 40):
+        ro, rl = OA.attention(f64(q[b:b + 1]), f64(k[b:b + 1]), f64(v[b:b + 1]), cfg.scale, False)
+        assert max_abs(f64(o[b:b + 1]), ro) <= O_TOL[q.dtype]
+        assert max_abs(lse[b:b + 1].double().numpy(), rl) <= LSE_TOL
+
+
+def _row_samples(rng, B, Hq, N, per_head, heads=None):
+    fixed = [0, 1, 63, 64, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1]
+    out = []
+    for h in (range(Hq) if heads is None else heads):
+        rows = fixed + list(rng.integers(0, N, per_head))
+        out.append((int(rng.integers(0, B)), h, [r for r in rows if 0 <= r < N]))
+    return out
+
+
+@pytest.mark.parametrize("name", ["gqa_causal_t8192", "mha_causal_t32768"])
+def test_config_long_causal_sampled(name):
+    cfg = DENSE_CONFIGS[name]
+    q, k, v = dense_inputs(cfg)
+    announce(cfg.name)
+    o, lse = run_fwd(q, k, v, cfg.scale, True)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(123)
+    check_dense_rows(o, lse, f64(q), f64(k), f64(v), cfg.scale, True,
+                     _row_samples(rng, cfg.B, cfg.Hq, cfg.N, 24), cfg.name)
