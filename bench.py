@@ -88,6 +88,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,6 +125,14 @@ def main(argv=None):
     def decode():
         attn_paged_decode(pd["q"], pd["k_cache"], pd["v_cache"], pd["block_table"], pd["ctx_lens"],
                           16, dcfg.scale, o=od, lse=lsed, workspace=ws, stream=stream)
+
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         prefill()

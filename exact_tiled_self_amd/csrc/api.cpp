@@ -103,7 +103,9 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
-    if ((long long)N * d >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "N * d must be below 2^31");
+    // per-head byte offsets (plus one tile of look-ahead) must fit 32 bits
+    if ((long long)N * d > (1LL << 31) - (1LL << 16))
+        return fail(ATTN_ERR_UNSUPPORTED, "N * d must be at most 2^31 - 2^16");
     const long long grid = (long long)B * Hq * ((N + 63) / 64);
     if (grid >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))

@@ -43,6 +43,25 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads beyond the range
+// return zero, so tile edges need no branches.  (Word 3 is the gfx9 raw
+// buffer format used for 32-bit data.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base must be wave-uniform).
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
+}
+
 // Wave-wide exchange with lane ^ mask (ds_bpermute based).
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
     return __shfl_xor(x, mask, 64);

@@ -5,27 +5,29 @@
 // rápida y fusión de operadores", section "Atención tipo FlashAttention y
 // atención paginada").  Every key position is translated through the table.
 //
-// Work split.  One workgroup per (sequence, kv head, 256-token split); each
-// of its 4 waves takes 4 consecutive logical blocks (64 tokens).  The G query
-// heads that share the kv head (grouped-query attention) form the rows of
-// the score tile, so the two products are genuine small matrix products and
-// run on MFMA (v_mfma_f32_16x16x32_bf16, G <= 16 rows):
+// Work split.  One workgroup per (sequence, kv head, 512-token split); each
+// of its 4 waves streams 8 consecutive logical blocks (128 tokens) in steps
+// of two blocks, with two register sets so that the loads of step j+1 are in
+// flight while step j computes, and keeps its own running state (m, l, u).
+// The G query heads that share the kv head (grouped-query attention) form
+// the rows of the score tile, so the two products are genuine small matrix
+// products and run on MFMA (v_mfma_f32_16x16x32_bf16, G <= 16 rows):
 //   * S^T = K Q^T: the lane's A operand is 8 dims of one key, loaded straight
-//     from the block in HBM; each lane ends up owning one query row
-//     (lane % 16) and 4 keys of each block.
-//   * O = P V: P comes from the lane's own score registers (keys 4g..4g+3 of
-//     two blocks); the V operand needs 8 keys of one dim per lane, so each
-//     lane loads a 16-byte row slice of 8 keys (coalesced: 16 lanes cover one
-//     256-byte row) and transposes the 8x8 block in registers with v_perm.
-//     Output dims are permuted (lane column n holds dims 8n..8n+7 across the
-//     8 MFMAs) so that those slices are contiguous.
-// Each wave's running state (m, l, u) is merged with the other waves' in
-// LDS by the rescale rule of the online softmax, and the workgroup writes one
-// fp32 partial state per query head to the workspace.  A second kernel
-// merges the partial states of a sequence in split order (deterministic):
-// M = max m_k, L = sum l_k e^(m_k - M), O = sum u_k e^(m_k - M) / L
-// ("FlashAttention" notes, section "No basta con promediar los resultados de
-// los bloques": each part enters with its own weight, not as an average).
+//     from the block; each lane ends up owning one query row (lane % 16) and
+//     4 keys of each block.
+//   * O^T = V^T P^T: P^T comes from the lane's own score registers (keys
+//     4g..4g+3 of both blocks); the V^T operand needs 8 keys of one dim per
+//     lane, so each lane loads 16-byte row slices of its 8 keys (coalesced:
+//     16 lanes cover one 256-byte row) and transposes the 8x8 block in
+//     registers with v_perm.  The output again has one query row per lane,
+//     so the rescale by e^(m - m') is lane-local.
+// The four waves' states are merged in LDS by the rescale rule of the online
+// softmax, and the workgroup writes one fp32 partial state per query head to
+// the workspace.  A second kernel merges the partial states of a sequence in
+// split order (deterministic): M = max m_k, L = sum l_k e^(m_k - M),
+// O = sum u_k e^(m_k - M) / L ("FlashAttention" notes, section "No basta con
+// promediar los resultados de los bloques": each part enters with its own
+// weight, not as an average).
 //
 // Slots past a sequence's length inside its last block are loaded (they are
 // inside the block) but their V rows are zeroed and their scores excluded
@@ -39,20 +41,26 @@ namespace attn {
 namespace {
 
 constexpr int DC_THREADS = 256;
-constexpr int DC_BLOCKS_PER_WAVE = 4;
-static_assert(4 * DC_BLOCKS_PER_WAVE * kDecodeBlock == kDecodeSplit, "split = 4 waves x 4 blocks");
+constexpr int DC_WAVE_BLOCKS = 8;        // 128 tokens per wave
+constexpr int DC_STEP_BLOCKS = 2;        // 32 tokens per pipeline step
+constexpr int DC_STEPS = DC_WAVE_BLOCKS / DC_STEP_BLOCKS;
+static_assert(4 * DC_WAVE_BLOCKS * kDecodeBlock == kDecodeSplit, "split = 4 waves x 8 blocks");
 
 template <int D>
 struct VRow;
 template <>
-struct VRow<128> { typedef u32x4 T; static constexpr int WORDS = 4; };
+struct VRow<128> { typedef u32x4 T; };
 template <>
-struct VRow<64> { typedef u32x2 T; static constexpr int WORDS = 2; };
+struct VRow<64> { typedef u32x2 T; };
 
+// Registers of one pipeline step (two blocks): K operands and V row slices.
 template <int D>
-__device__ __forceinline__ typename VRow<D>::T ld_vrow(const uint16_t* p) {
-    return *reinterpret_cast<const typename VRow<D>::T*>(p);
-}
+struct StepRegs {
+    u32x4 k[DC_STEP_BLOCKS][D / 32];
+    typename VRow<D>::T v[8];
+    int phys[DC_STEP_BLOCKS];
+    bool valid[DC_STEP_BLOCKS];
+};
 
 template <int D>
 __global__ void __launch_bounds__(DC_THREADS)
@@ -61,7 +69,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const int32_t* __restrict__ ctx_lens, float* __restrict__ ws, int Hq,
                       int Hkv, int max_blocks, int num_blocks, int nsplit, float c, int negate) {
     constexpr int KS = D / 32;              // MFMA k-steps over the head dim
-    constexpr int DPL = D / 16;             // output dims per lane column
+    constexpr int DPL = D / 16;             // dims per lane column of an MFMA
     using VT = typename VRow<D>::T;
 
     __shared__ float sm_m[4][16];
@@ -79,50 +87,13 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
     const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
-    const int fb = split * (kDecodeSplit / kDecodeBlock) + wave * DC_BLOCKS_PER_WAVE;
-
-    // Physical blocks of this wave (wave-uniform).
-    int phys[DC_BLOCKS_PER_WAVE];
-    bool valid[DC_BLOCKS_PER_WAVE];
+    const int fb = split * (kDecodeSplit / kDecodeBlock) + wave * DC_WAVE_BLOCKS;
+    const int wblocks = min(max(nblk - fb, 0), DC_WAVE_BLOCKS);
+    const int nsteps = (wblocks + DC_STEP_BLOCKS - 1) / DC_STEP_BLOCKS;
     bool bad = false;
-#pragma unroll
-    for (int i = 0; i < DC_BLOCKS_PER_WAVE; ++i) {
-        const int lb = fb + i;
-        valid[i] = lb < nblk;
-        int p = valid[i] ? table[(size_t)s * max_blocks + lb] : 0;
-        if (valid[i] && (p < 0 || p >= num_blocks)) {
-            bad = true;
-            valid[i] = false;
-            p = 0;
-        }
-        phys[i] = p;
-    }
 
-    // K operand loads: key l16 of block i, dims 8*(4ks + grp) .. +7.
-    u32x4 kr[DC_BLOCKS_PER_WAVE][KS];
-#pragma unroll
-    for (int i = 0; i < DC_BLOCKS_PER_WAVE; ++i)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kr[i][ks] = valid[i] ? ld16(kc + (((size_t)phys[i] * Hkv + g) * kDecodeBlock + l16) * D +
-                                        8 * (4 * ks + grp))
-                                 : u32x4{0u, 0u, 0u, 0u};
-    // V operand loads: for block pair bp, entry i8 -> block 2bp + i8/4, key
-    // 4*grp + i8%4, dims DPL*l16 .. +DPL-1.
-    VT vr[2][8];
-#pragma unroll
-    for (int bp = 0; bp < 2; ++bp)
-#pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-            const int blk = 2 * bp + (i8 >> 2);
-            const int key = 4 * grp + (i8 & 3);
-            VT w = {};
-            if (valid[blk])
-                w = ld_vrow<D>(vc + (((size_t)phys[blk] * Hkv + g) * kDecodeBlock + key) * D + DPL * l16);
-            vr[bp][i8] = w;
-        }
-
-    // Q operand: query row l16 (head g*G + l16 when l16 < G), same dims as K.
+    // Q operand (B of S^T = K Q^T): query row l16 (head g*G + l16 when l16 < G),
+    // dims 8*(4ks + grp) .. +7.
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -132,87 +103,133 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // Scores.
-    f32x4 sacc[DC_BLOCKS_PER_WAVE];
+    auto load_step = [&](StepRegs<D>& R, int st) {
 #pragma unroll
-    for (int i = 0; i < DC_BLOCKS_PER_WAVE; ++i) {
-        sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i][ks]),
-                                                              qf[ks], sacc[i], 0, 0, 0);
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < DC_BLOCKS_PER_WAVE; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tok = (fb + i) * kDecodeBlock + 4 * grp + r;
-            const bool ok = valid[i] && tok < ctx;
-            sacc[i][r] = ok ? sacc[i][r] : kNegInf;
-            mx = fmaxf(mx, sacc[i][r]);
+        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
+            const int lb = fb + st * DC_STEP_BLOCKS + bi;
+            bool ok = lb < nblk;
+            int p = ok ? table[(size_t)s * max_blocks + lb] : 0;
+            if (ok && (p < 0 || p >= num_blocks)) {
+                bad = true;
+                ok = false;
+                p = 0;
+            }
+            R.phys[bi] = p;
+            R.valid[bi] = ok;
         }
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float m_use = (mx == kNegInf) ? 0.f : mx;
-    const float mc = m_use * c;
-    float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < DC_BLOCKS_PER_WAVE; ++i)
+        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
+            const uint16_t* kb = kc + (((size_t)R.phys[bi] * Hkv + g) * kDecodeBlock + l16) * D;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float sv = sacc[i][r];
-            const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
-            sacc[i][r] = p;
-            lsum += p;
+            for (int ks = 0; ks < KS; ++ks)
+                R.k[bi][ks] = R.valid[bi] ? ld16(kb + 8 * (4 * ks + grp)) : u32x4{0u, 0u, 0u, 0u};
         }
-    lsum += xor_shfl(lsum, 16);
-    lsum += xor_shfl(lsum, 32);
+#pragma unroll
+        for (int i8 = 0; i8 < 8; ++i8) {
+            const int bi = i8 >> 2;
+            const uint16_t* vr = vc + (((size_t)R.phys[bi] * Hkv + g) * kDecodeBlock + 4 * grp + (i8 & 3)) * D;
+            R.v[i8] = R.valid[bi] ? *reinterpret_cast<const VT*>(vr + DPL * l16) : VT{};
+        }
+    };
 
-    // O = P V over the two block pairs.
+    float m_run = kNegInf, l_run = 0.f;
     f32x4 oacc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_step = [&](StepRegs<D>& R, int st) {
+        const int tok0 = (fb + st * DC_STEP_BLOCKS) * kDecodeBlock;
+        f32x4 sacc[DC_STEP_BLOCKS];
 #pragma unroll
-    for (int bp = 0; bp < 2; ++bp) {
-        // zero the V rows of positions past the length (NaN-safe)
+        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
+            sacc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-            const int blk = 2 * bp + (i8 >> 2);
-            const int tok = (fb + blk) * kDecodeBlock + 4 * grp + (i8 & 3);
-            if (tok >= ctx) vr[bp][i8] = VT{};
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.k[bi][ks]),
+                                                                   qf[ks], sacc[bi], 0, 0, 0);
         }
-        bf16x8 pa;
+        // lane: query row l16, keys 4*grp + r of each block
+        float mx = kNegInf;
+#pragma unroll
+        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = R.valid[bi] && (tok0 + bi * kDecodeBlock + 4 * grp + r) < ctx;
+                sacc[bi][r] = ok ? sacc[bi][r] : kNegInf;
+                mx = fmaxf(mx, sacc[bi][r]);
+            }
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_use) * c);
+        const float mc = m_use * c;
+        float lsum = 0.f;
+#pragma unroll
+        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sv = sacc[bi][r];
+                const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+                sacc[bi][r] = p;
+                lsum += p;
+            }
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+        // P^T operand: row l16, keys (4grp..4grp+3) of block 0 then of block 1
+        bf16x8 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pa[i] = (__bf16)sacc[2 * bp][i];
-            pa[4 + i] = (__bf16)sacc[2 * bp + 1][i];
+            pb[i] = (__bf16)sacc[0][i];
+            pb[4 + i] = (__bf16)sacc[1][i];
         }
+        // V rows of positions past the length are zeroed (NaN-safe)
+#pragma unroll
+        for (int i8 = 0; i8 < 8; ++i8)
+            if (!(R.valid[i8 >> 2] && (tok0 + (i8 >> 2) * kDecodeBlock + 4 * grp + (i8 & 3)) < ctx))
+                R.v[i8] = VT{};
+        // O^T += V^T P^T: A operand = 8 keys of dim DPL*l16 + j (8x8 register transpose)
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
             const int w = j >> 1;
             const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
             u32x4 t;
-            t.x = __builtin_amdgcn_perm(vr[bp][1][w], vr[bp][0][w], sel);
-            t.y = __builtin_amdgcn_perm(vr[bp][3][w], vr[bp][2][w], sel);
-            t.z = __builtin_amdgcn_perm(vr[bp][5][w], vr[bp][4][w], sel);
-            t.w = __builtin_amdgcn_perm(vr[bp][7][w], vr[bp][6][w], sel);
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, t),
+            t.x = __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], sel);
+            t.y = __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], sel);
+            t.z = __builtin_amdgcn_perm(R.v[5][w], R.v[4][w], sel);
+            t.w = __builtin_amdgcn_perm(R.v[7][w], R.v[6][w], sel);
+            oacc[j] *= alpha;
+            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t), pb,
                                                               oacc[j], 0, 0, 0);
+        }
+    };
+
+    // Two register sets, ping-pong: the loads of step st+1 are in flight
+    // while step st computes.
+    StepRegs<D> ra, rb;
+    if (nsteps > 0) load_step(ra, 0);
+#pragma unroll 1
+    for (int st = 0; st < nsteps; st += 2) {
+        if (st + 1 < nsteps) load_step(rb, st + 1);
+        compute_step(ra, st);
+        if (st + 1 < nsteps) {
+            if (st + 2 < nsteps) load_step(ra, st + 2);
+            compute_step(rb, st + 1);
         }
     }
 
-    // Merge the four waves' states in LDS.
+    // lane: row l16, dims DPL*(4grp + r) + j.  Merge the four waves in LDS.
+    l_run += xor_shfl(l_run, 16);
+    l_run += xor_shfl(l_run, 32);
     if (grp == 0) {
-        sm_m[wave][l16] = mx;
-        sm_l[wave][l16] = bad ? __builtin_nanf("") : lsum;
+        sm_m[wave][l16] = m_run;
+        sm_l[wave][l16] = bad ? __builtin_nanf("") : l_run;
     }
+    if (l16 < G) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * grp + r;
-        if (row < G)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) sm_o[wave][row][DPL * l16 + j] = oacc[j][r];
+            for (int j = 0; j < DPL; ++j) sm_o[wave][l16][DPL * (4 * grp + r) + j] = oacc[j][r];
     }
     __syncthreads();
 
@@ -238,20 +255,24 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
 }
 
-// One wave per (sequence, query head): merge the sequence's split states in
-// split order.
+// One workgroup per (kv head, sequence): merge the sequence's split states
+// in split order for the G query heads of the group.  The splits' (m, l)
+// pairs are fetched in parallel into LDS (in chunks of kCombineChunk
+// splits), the per-row maximum and sum are formed there, and every thread
+// then accumulates its (row, dim) outputs over the splits.
+constexpr int kCombineChunk = 64;
+
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ ctx_lens,
                       uint16_t* __restrict__ o, float* __restrict__ lse, int S, int Hq, int Hkv,
                       int max_blocks, int nsplit, float c) {
-    constexpr int DPT = D / 64;             // dims per lane
-    const int lane = threadIdx.x & 63;
-    const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (sh >= S * Hq) return;
-    const int s = sh / Hq, h = sh - s * Hq;
+    __shared__ float sm_mk[kCombineChunk][16];
+    __shared__ float sm_lk[kCombineChunk][16];
+    __shared__ float sm_M[16], sm_L[16];
+    const int g = blockIdx.x, s = blockIdx.y;
     const int G = Hq / Hkv;
-    const int g = h / G, n = h - g * G;
+    const int tid = threadIdx.x;
     const int cap = max_blocks * kDecodeBlock;
     int ctx = ctx_lens[s];
     const bool bad = ctx < 0 || ctx > cap;
@@ -260,35 +281,58 @@ decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ 
     const size_t stride = (size_t)G * (D + 2);
     const float* base = ws + (size_t)(s * Hkv + g) * nsplit * stride;
 
-    float M = kNegInf;
-    for (int kk = 0; kk < nsp; ++kk) M = fmaxf(M, base[kk * stride + n]);
-    float L = 0.f, U[DPT];
-#pragma unroll
-    for (int t = 0; t < DPT; ++t) U[t] = 0.f;
-    for (int kk = 0; kk < nsp; ++kk) {
-        const float* p = base + kk * stride;
-        const float mk = p[n];
-        const float f = (mk == kNegInf) ? 0.f : fast_exp2((mk - M) * c);
-        L = fmaf(f, p[G + n], L);
-#pragma unroll
-        for (int t = 0; t < DPT; ++t) U[t] = fmaf(f, p[2 * G + n * D + lane * DPT + t], U[t]);
+    // Per-row maximum M, then L = sum_k l_k e^(m_k - M), chunk by chunk.
+    float M = kNegInf, L = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int k0 = 0; k0 < nsp; k0 += kCombineChunk) {
+            const int nk = min(kCombineChunk, nsp - k0);
+            __syncthreads();
+            for (int e = tid; e < nk * G; e += 256) {
+                const int kk = e / G, row = e - kk * G;
+                sm_mk[kk][row] = base[(k0 + kk) * stride + row];
+                sm_lk[kk][row] = base[(k0 + kk) * stride + G + row];
+            }
+            __syncthreads();
+            if (tid < G) {
+                for (int kk = 0; kk < nk; ++kk) {
+                    const float mk = sm_mk[kk][tid];
+                    if (pass == 0) {
+                        M = fmaxf(M, mk);
+                    } else {
+                        const float f = (mk == kNegInf) ? 0.f : fast_exp2((mk - M) * c);
+                        L = fmaf(f, sm_lk[kk][tid], L);
+                    }
+                }
+            }
+        }
     }
+    if (tid < G) {
+        sm_M[tid] = M;
+        sm_L[tid] = L;
+    }
+    __syncthreads();
+
     const float nan = __builtin_nanf("");
-    const float inv = (L > 0.f) ? 1.f / L : (L == 0.f ? 0.f : nan);
-    uint16_t* orow = o + ((size_t)s * Hq + h) * D + lane * DPT;
-    if constexpr (DPT == 2) {
-        const float a = bad ? nan : U[0] * inv, b2 = bad ? nan : U[1] * inv;
-        *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(a, b2);
-    } else {
-        const float a = bad ? nan : U[0] * inv;
-        typedef __bf16 bf1;
-        bf1 x = (bf1)a;
-        *orow = __builtin_bit_cast(uint16_t, x);
-    }
-    if (lse != nullptr && lane == 0) {
-        float lv = (M == kNegInf) ? kNegInf : (M * c + log2f(L)) * kLn2;
-        if (bad || L != L) lv = nan;
-        lse[(size_t)s * Hq + h] = lv;
+    for (int e = tid; e < G * D; e += 256) {
+        const int row = e / D, dim = e - row * D;
+        const float Mr = sm_M[row], Lr = sm_L[row];
+        float U = 0.f;
+#pragma unroll 8
+        for (int kk = 0; kk < nsp; ++kk) {
+            const float* p = base + kk * stride;
+            const float mk = p[row];
+            const float f = (mk == kNegInf) ? 0.f : fast_exp2((mk - Mr) * c);
+            U = fmaf(f, p[2 * G + e], U);
+        }
+        const float inv = (Lr > 0.f) ? 1.f / Lr : (Lr == 0.f ? 0.f : nan);
+        const float val = bad ? nan : U * inv;
+        const __bf16 bv = (__bf16)val;
+        o[((size_t)s * Hq + g * G + row) * D + dim] = __builtin_bit_cast(uint16_t, bv);
+        if (lse != nullptr && dim == 0) {
+            float lv = (Mr == kNegInf) ? kNegInf : (Mr * c + log2f(Lr)) * kLn2;
+            if (bad || Lr != Lr) lv = nan;
+            lse[(size_t)s * Hq + g * G + row] = lv;
+        }
     }
 }
 
@@ -302,7 +346,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        a.workspace, a.Hq, a.Hkv, a.max_blocks, a.num_blocks, nsplit, a.c, a.negate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2((unsigned)((a.S * a.Hq + 3) / 4)), b2(256);
+    const dim3 g2((unsigned)a.Hkv, (unsigned)a.S), b2(256);
     hipLaunchKernelGGL((decode_combine_kernel<D>), g2, b2, 0, stream, a.workspace, a.ctx_lens,
                        static_cast<uint16_t*>(a.o), a.lse, a.S, a.Hq, a.Hkv, a.max_blocks, nsplit, a.c);
     return hipGetLastError();

@@ -27,7 +27,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 // Paged decode: keys are processed in splits of kDecodeSplit tokens, each
 // producing an fp32 partial state (m, l, u) per query head in the workspace,
 // which a second kernel merges.
-constexpr int kDecodeSplit = 256;
+constexpr int kDecodeSplit = 512;
 constexpr int kDecodeBlock = 16;   // tokens per KV-cache block
 
 struct DecodeArgs {

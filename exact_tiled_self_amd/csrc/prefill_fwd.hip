@@ -20,8 +20,14 @@
 //     (converted to bf16); V^T is read from LDS, where the staging code
 //     stores V transposed with keys 4..7 and 8..11 of every 16-key group
 //     swapped, which is exactly the key order of the accumulator lanes.
-//   * K/V tiles are double-buffered in LDS; the global loads of tile j+1
-//     are issued before the MFMA work on tile j.
+//   * K/V tiles are double-buffered in LDS; the loads of tile j+1 are issued
+//     before the MFMA work on tile j.  K goes straight from memory into LDS
+//     (buffer_load ... lds, 16-byte chunks of each row XOR-swizzled so the
+//     operand fetches are free of bank conflicts); V passes through registers
+//     to be stored transposed.  Buffer resources bound every load by the
+//     head's extent, so rows past N read as zero without branches.
+//   * The running maximum is raised lazily: only when a tile's maximum
+//     exceeds it by more than 2^8 in weight does the wave rescale l and u.
 //   * Causal: tiles entirely above the diagonal are never visited, the q
 //     tiles are dispatched heaviest first, and a wave whose rows all lie
 //     before a tile skips its arithmetic for it.
@@ -41,23 +47,36 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 
 template <int D>
 struct PfLayout {
-    static constexpr int KSTR = D + 8;          // bf16 per K row in LDS (16-B pad)
+    static constexpr int CPR = D / 8;           // 16-byte chunks per K row
     static constexpr int VSTR = PF_BN + 8;      // bf16 per V^T row in LDS (16-B pad)
-    static constexpr int KELEMS = PF_BN * KSTR;
+    static constexpr int KELEMS = PF_BN * D;    // K tile, rows XOR-swizzled, no pad
     static constexpr int VELEMS = D * VSTR;
-    static constexpr int BUF = KELEMS + VELEMS; // one pipeline stage
-    static constexpr int KCHUNKS = PF_BN * D / 8 / PF_THREADS;  // 16-B K chunks per thread
+    static constexpr int BUF = KELEMS + VELEMS; // one pipeline stage (bf16 elements)
+    static constexpr int KINST = PF_BN * CPR / PF_THREADS;     // K load-to-LDS per thread
     static constexpr int VKPT = PF_BN * D / 8 / PF_THREADS;     // keys per thread (V)
     static constexpr int VKGROUPS = PF_BN / VKPT;
-    static_assert(KCHUNKS * PF_THREADS * 8 == PF_BN * D, "K tile split");
+    static_assert(KINST * PF_THREADS == PF_BN * CPR, "K tile split");
     static_assert(VKPT == 2 || VKPT == 4, "V staging handles 2 or 4 keys per thread");
 };
+
+// XOR swizzle of the 16-byte chunks of K row r, so that the 16 rows read by
+// one MFMA operand fetch hit 16 different bank groups.
+template <int CPR>
+__device__ __forceinline__ int kswz(int r) {
+    return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
+}
 
 // Position of key x (within a 16-key group) in the V^T layout: bits 2 and 3
 // exchanged.  It is its own inverse.
 __device__ __forceinline__ int swap23(int x) {
     return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
+
+// A tile raises the running maximum only when some row's new maximum exceeds
+// it by more than 2^8 in weight: below that the old maximum stays the
+// reference (weights up to 256 are exact in fp32 and bf16 range) and the
+// numerator needs no rescale.  u / l is unchanged by the choice of reference.
+constexpr float kLazyLog2 = 8.0f;
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -78,21 +97,22 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int bh = wg % BH;
     const int b = bh / Hq, h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
-    const uint16_t* qh = q + (size_t)bh * N * D;
-    const uint16_t* kh = k + ((size_t)b * Hkv + g) * N * D;
-    const uint16_t* vh = v + ((size_t)b * Hkv + g) * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
 
     const int q0 = qt * PF_BM;
     const int wrow0 = q0 + wave * 32;
     const int myrow = wrow0 + l32;
     const bool wave_active = wrow0 < N;
 
-    // Q as the B operand of S^T = K Q^T: row `myrow`, dims 16*ks + 8*hi .. +7.
+    // Q as the B operand of S^T = K Q^T: row `myrow`, dims 16*ks + 8*hi .. +7
+    // (rows past N read as zero).
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (myrow < N) w = ld16(qh + (size_t)myrow * D + ks * 16 + hi * 8);
+        u32x4 w = buf_ld16(qrs, (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2);
         if (negate) w = neg_bf16x8(w);
         qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
@@ -100,36 +120,34 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int row_end = min(q0 + PF_BM, N);
     const int n_kt = CAUSAL ? (row_end + PF_BN - 1) / PF_BN : (N + PF_BN - 1) / PF_BN;
 
-    u32x4 kreg[L::KCHUNKS];
+    // K staging: load-to-LDS unit p = (i * waves + wave) * 64 + lane holds the
+    // 16-byte chunk (row p / CPR, chunk (p % CPR) ^ swz(row)) of the tile.
+    uint32_t koff[L::KINST];
+#pragma unroll
+    for (int i = 0; i < L::KINST; ++i) {
+        const int p = (i * PF_WAVES + wave) * 64 + lane;
+        const int r = p / L::CPR;
+        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
+        koff[i] = (uint32_t)(r * D + cc * 8) * 2;
+    }
+    // V staging through registers (stored transposed): keys vkg*VKPT + i, dims vdc*8 .. +7.
+    const int vkg = tid % L::VKGROUPS;
+    const int vdc = tid / L::VKGROUPS;
+    const uint32_t voff = (uint32_t)((vkg * L::VKPT) * D + vdc * 8) * 2;
     u32x4 vreg[L::VKPT];
-    const int vkg = tid % L::VKGROUPS;       // this thread's key group (V staging)
-    const int vdc = tid / L::VKGROUPS;       // this thread's 8-dim chunk (V staging)
 
-    auto load_tile = [&](int kt) {
-        const int k0 = kt * PF_BN;
+    auto issue_loads = [&](int kt, int buf) {
+        const uint32_t t0 = (uint32_t)kt * PF_BN * D * 2;
+        uint16_t* Ks = smem + buf * L::BUF;
 #pragma unroll
-        for (int i = 0; i < L::KCHUNKS; ++i) {
-            const int cid = tid + PF_THREADS * i;
-            const int r = cid / (D / 8), cc = (cid % (D / 8)) * 8;
-            const int key = k0 + r;
-            kreg[i] = (key < N) ? ld16(kh + (size_t)key * D + cc) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < L::KINST; ++i)
+            buf_ld16_lds(krs, Ks + (i * PF_WAVES + wave) * 64 * 8, t0 + koff[i]);
 #pragma unroll
-        for (int i = 0; i < L::VKPT; ++i) {
-            const int key = k0 + vkg * L::VKPT + i;
-            vreg[i] = (key < N) ? ld16(vh + (size_t)key * D + vdc * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < L::VKPT; ++i) vreg[i] = buf_ld16(vrs, t0 + voff + (uint32_t)(i * D * 2));
     };
 
-    auto store_tile = [&](int buf) {
-        uint16_t* Ks = smem + buf * L::BUF;
-        uint16_t* Vt = Ks + L::KELEMS;
-#pragma unroll
-        for (int i = 0; i < L::KCHUNKS; ++i) {
-            const int cid = tid + PF_THREADS * i;
-            const int r = cid / (D / 8), cc = (cid % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(Ks + r * L::KSTR + cc) = kreg[i];
-        }
+    auto store_v = [&](int buf) {
+        uint16_t* Vt = smem + buf * L::BUF + L::KELEMS;
         const int pos = swap23(vkg * L::VKPT);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -153,13 +171,15 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    load_tile(0);
-    store_tile(0);
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    store_v(0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < n_kt) load_tile(kt + 1);
+        const bool more = kt + 1 < n_kt;
+        if (more) issue_loads(kt + 1, buf ^ 1);
         const int k0 = kt * PF_BN;
         const bool compute = wave_active && (!CAUSAL || k0 <= wrow0 + 31);
         if (compute) {
@@ -176,8 +196,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < PF_BN / 32; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        Ks + (kb * 32 + l32) * L::KSTR + ks * 16 + hi * 8);
+                    const int r = kb * 32 + l32;
+                    const int cc = (ks * 2 + hi) ^ kswz<L::CPR>(r);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + r * D + cc * 8);
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
                 }
             }
@@ -202,18 +223,29 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
             }
             mx = fmaxf(mx, xor_shfl(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_use) * c);
-            const float mc = m_use * c;
+
+            // Lazy rescale: a wave-uniform branch taken only when some row's
+            // maximum grew by more than 2^kLazyLog2 (always on the first tile).
+            const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m_run = m_new;
+            }
+            const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
             float lsum = 0.f;
             if (need_mask) {
 #pragma unroll
                 for (int kb = 0; kb < PF_BN / 32; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float s = sacc[kb][r];
-                        const float p = (s == kNegInf) ? 0.f : fast_exp2(fmaf(s, c, -mc));
+                        const float sv = sacc[kb][r];
+                        const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
                         sacc[kb][r] = p;
                         lsum += p;
                     }
@@ -227,12 +259,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                         lsum += p;
                     }
             }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
+            l_run += lsum;
 
             // O^T += V^T P^T, 16 keys per MFMA.
 #pragma unroll
@@ -249,7 +276,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 }
             }
         }
-        if (kt + 1 < n_kt) store_tile(buf ^ 1);
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);     // tile kt+1: K in LDS, V in registers
+            store_v(buf ^ 1);
+        }
         __syncthreads();
     }
 
@@ -268,7 +298,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 *reinterpret_cast<u32x2*>(orow + dim0) = w;
             }
         if (lse != nullptr && hi == 0)
-            lse[(size_t)bh * N + myrow] = (m_run * c + __log2f(l_tot)) * kLn2;
+            lse[(size_t)bh * N + myrow] = (m_run * c + log2f(l_tot)) * kLn2;
     }
 }
 
@@ -372,7 +402,7 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
             *reinterpret_cast<f32x4*>(orow + i) =
                 f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
         if (lse != nullptr && part == 0)
-            lse[(size_t)bh * N + myrow] = (m_run * c + __log2f(l_run)) * kLn2;
+            lse[(size_t)bh * N + myrow] = (m_run * c + log2f(l_run)) * kLn2;
     }
 }
 

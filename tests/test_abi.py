@@ -104,8 +104,8 @@ def test_decode_rejects_before_any_launch(lib, kw, status):
 
 
 def test_workspace_size(lib):
-    # fp32 partial state (m, l, u[d]) per query head and 256-token split
-    assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == 64 * 12 * 32 * 130 * 4
+    # fp32 partial state (m, l, u[d]) per query head and 512-token split
+    assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == 64 * 12 * 16 * 130 * 4
     assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 16) == 1 * 1 * 1 * 66 * 4
     assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 32) == 0
     assert lib.attn_paged_decode_workspace_size(0, 1, 64, 1, 16) == 0
