@@ -72,7 +72,10 @@ def profiled_traffic(profile: str, sources) -> float | None:
         return None
     h = hashlib.sha256()
     for f in sources:
-        h.update(open(os.path.join(ROOT, "exact_tiled_self_amd", "csrc", f), "rb").read())
+        src = os.path.join(ROOT, "exact_tiled_self_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
     traffic, digest = None, None
     for line in open(path):
         if line.startswith("traffic_bytes_per_launch:"):
@@ -237,7 +240,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("prefill_bf16_d128_causal_gqa_t8192",
-                                                 ["prefill_fwd.hip", "common.h", "internal.h"]),
+                                                 ["prefill_bf16.hip", "common.h", "internal.h"]),
                      "algorithmic_bytes": prefill_bytes(pcfg),
                      "kernel": "prefill_bf16_kernel<128, causal>",
                      "per_launch": {"flops": pf, "avg_us": round(pre_avg * 1e3, 2),

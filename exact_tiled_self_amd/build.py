@@ -22,12 +22,16 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "prefill_fwd.hip", "decode_paged.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip"]
 
 # Device-code flags: gfx950 only; packed fp32 instructions disabled.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
+
+# Per-source additions.  The bf16 prefill never produces or consumes a NaN
+# (masked scores are -inf), so maxima need no NaN canonicalisation.
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -38,23 +42,44 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, out: str = LIB_PATH) -> str:
-    """Compile every source into `out` and return its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".libattn.", suffix=".so.tmp", dir=os.path.dirname(out))
-    os.close(fd)
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass reports the device-only feature flag as unknown; drop that noise.
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if noise not in ln]
-    if proc.returncode != 0:
-        os.unlink(tmp)
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, out)
+    """Compile every source (in parallel, each with its own flags), link
+    them into `out` and return its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    noise = "is not a recognized feature for this target"   # hipcc host-pass noise
+    tmpdir = tempfile.mkdtemp(prefix=".attn_build.", dir=os.path.dirname(out))
+    try:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC,
+                   "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            proc = subprocess.run(cmd, capture_output=True, text=True)
+            msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if noise not in ln]
+            return src, obj, proc.returncode, msgs
+
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        errors = [f"{src}:\n" + "\n".join(msgs) for src, _, rc, msgs in results if rc != 0]
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        if verbose:
+            for src, _, _, msgs in results:
+                if msgs:
+                    print("\n".join(msgs))
+        fd, tmp = tempfile.mkstemp(prefix=".libattn.", suffix=".so.tmp", dir=os.path.dirname(out))
+        os.close(fd)
+        cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp, *[obj for _, obj, _, _ in results]]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            os.unlink(tmp)
+            raise RuntimeError("link failed:\n" + proc.stdout + proc.stderr)
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return out
 
 
