@@ -84,13 +84,22 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int nsplit_s = (ctx + kDecodeSplit - 1) / kDecodeSplit;
     if (split >= nsplit_s) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: keep the block-table walk in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
     const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
     const int fb = split * (kDecodeSplit / kDecodeBlock) + wave * DC_WAVE_BLOCKS;
     const int wblocks = min(max(nblk - fb, 0), DC_WAVE_BLOCKS);
     const int nsteps = (wblocks + DC_STEP_BLOCKS - 1) / DC_STEP_BLOCKS;
-    bool bad = false;
+
+    // The wave's table entries, fetched once up front (lane j holds entry
+    // fb + j), so that no K/V load waits behind a table read; entries outside
+    // [0, num_blocks) are not followed (the sequence's output becomes NaN).
+    int tab = 0;
+    if (lane < wblocks) tab = table[(size_t)s * max_blocks + fb + lane];
+    const bool tab_ok = lane < wblocks && tab >= 0 && tab < num_blocks;
+    const uint64_t valid_mask = __builtin_amdgcn_ballot_w64(tab_ok);
+    const bool bad = __builtin_amdgcn_ballot_w64(lane < wblocks && !tab_ok) != 0;
 
     // Q operand (B of S^T = K Q^T): query row l16 (head g*G + l16 when l16 < G),
     // dims 8*(4ks + grp) .. +7.
@@ -106,15 +115,9 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     auto load_step = [&](StepRegs<D>& R, int st) {
 #pragma unroll
         for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
-            const int lb = fb + st * DC_STEP_BLOCKS + bi;
-            bool ok = lb < nblk;
-            int p = ok ? table[(size_t)s * max_blocks + lb] : 0;
-            if (ok && (p < 0 || p >= num_blocks)) {
-                bad = true;
-                ok = false;
-                p = 0;
-            }
-            R.phys[bi] = p;
+            const int j = st * DC_STEP_BLOCKS + bi;            // block index within the wave
+            const bool ok = (valid_mask >> j) & 1;
+            R.phys[bi] = ok ? __builtin_amdgcn_readlane(tab, j) : 0;
             R.valid[bi] = ok;
         }
 #pragma unroll
@@ -255,24 +258,20 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
 }
 
-// One workgroup per (kv head, sequence): merge the sequence's split states
-// in split order for the G query heads of the group.  The splits' (m, l)
-// pairs are fetched in parallel into LDS (in chunks of kCombineChunk
-// splits), the per-row maximum and sum are formed there, and every thread
-// then accumulates its (row, dim) outputs over the splits.
-constexpr int kCombineChunk = 64;
-
+// One workgroup per (query head, sequence), one thread per output dim:
+// merge the sequence's split states for that head in split order (fixed
+// order, so the result is deterministic):  M = max m_k,
+// L = sum l_k e^(m_k - M), O = sum u_k e^(m_k - M) / L, lse = M + ln L.
+// Each wave reads the splits' (m_k, l_k) with one load per lane (split k in
+// lane k), reduces them across lanes, and then issues all the u_k loads of
+// its dim at once.
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D)
 decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ ctx_lens,
                       uint16_t* __restrict__ o, float* __restrict__ lse, int S, int Hq, int Hkv,
                       int max_blocks, int nsplit, float c) {
-    __shared__ float sm_mk[kCombineChunk][16];
-    __shared__ float sm_lk[kCombineChunk][16];
-    __shared__ float sm_M[16], sm_L[16];
-    const int g = blockIdx.x, s = blockIdx.y;
-    const int G = Hq / Hkv;
-    const int tid = threadIdx.x;
+    const int h = blockIdx.x, s = blockIdx.y, dim = threadIdx.x, lane = dim & 63;
+    const int G = Hq / Hkv, g = h / G, row = h - g * G;
     const int cap = max_blocks * kDecodeBlock;
     int ctx = ctx_lens[s];
     const bool bad = ctx < 0 || ctx > cap;
@@ -281,58 +280,48 @@ decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ 
     const size_t stride = (size_t)G * (D + 2);
     const float* base = ws + (size_t)(s * Hkv + g) * nsplit * stride;
 
-    // Per-row maximum M, then L = sum_k l_k e^(m_k - M), chunk by chunk.
-    float M = kNegInf, L = 0.f;
-    for (int pass = 0; pass < 2; ++pass) {
-        for (int k0 = 0; k0 < nsp; k0 += kCombineChunk) {
-            const int nk = min(kCombineChunk, nsp - k0);
-            __syncthreads();
-            for (int e = tid; e < nk * G; e += 256) {
-                const int kk = e / G, row = e - kk * G;
-                sm_mk[kk][row] = base[(k0 + kk) * stride + row];
-                sm_lk[kk][row] = base[(k0 + kk) * stride + G + row];
+    // M over all splits, 64 per pass
+    float M = kNegInf;
+    for (int k0 = 0; k0 < nsp; k0 += 64) {
+        const float mk = (k0 + lane < nsp) ? base[(k0 + lane) * stride + row] : kNegInf;
+        float mx = mk;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        M = fmaxf(M, mx);
+    }
+    float L = 0.f, U = 0.f;
+    for (int k0 = 0; k0 < nsp; k0 += 64) {
+        const bool in = k0 + lane < nsp;
+        const float mk = in ? base[(k0 + lane) * stride + row] : kNegInf;
+        const float lk = in ? base[(k0 + lane) * stride + G + row] : 0.f;
+        const float fk = (mk == kNegInf) ? 0.f : fast_exp2((mk - M) * c);
+        float lw = fk * lk;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off, 64);
+        L += lw;
+        const int nk = min(64, nsp - k0);
+        // u loads in groups of 16, all issued before they are summed (in split order)
+        for (int j0 = 0; j0 < nk; j0 += 16) {
+            float uv[16], fw[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int kk = min(j0 + j, nk - 1);
+                fw[j] = (j0 + j < nk) ? __shfl(fk, kk, 64) : 0.f;
+                uv[j] = base[(k0 + kk) * stride + 2 * G + row * D + dim];
             }
-            __syncthreads();
-            if (tid < G) {
-                for (int kk = 0; kk < nk; ++kk) {
-                    const float mk = sm_mk[kk][tid];
-                    if (pass == 0) {
-                        M = fmaxf(M, mk);
-                    } else {
-                        const float f = (mk == kNegInf) ? 0.f : fast_exp2((mk - M) * c);
-                        L = fmaf(f, sm_lk[kk][tid], L);
-                    }
-                }
-            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) U = fmaf(fw[j], uv[j], U);
         }
     }
-    if (tid < G) {
-        sm_M[tid] = M;
-        sm_L[tid] = L;
-    }
-    __syncthreads();
-
     const float nan = __builtin_nanf("");
-    for (int e = tid; e < G * D; e += 256) {
-        const int row = e / D, dim = e - row * D;
-        const float Mr = sm_M[row], Lr = sm_L[row];
-        float U = 0.f;
-#pragma unroll 8
-        for (int kk = 0; kk < nsp; ++kk) {
-            const float* p = base + kk * stride;
-            const float mk = p[row];
-            const float f = (mk == kNegInf) ? 0.f : fast_exp2((mk - Mr) * c);
-            U = fmaf(f, p[2 * G + e], U);
-        }
-        const float inv = (Lr > 0.f) ? 1.f / Lr : (Lr == 0.f ? 0.f : nan);
-        const float val = bad ? nan : U * inv;
-        const __bf16 bv = (__bf16)val;
-        o[((size_t)s * Hq + g * G + row) * D + dim] = __builtin_bit_cast(uint16_t, bv);
-        if (lse != nullptr && dim == 0) {
-            float lv = (Mr == kNegInf) ? kNegInf : (Mr * c + log2f(Lr)) * kLn2;
-            if (bad || Lr != Lr) lv = nan;
-            lse[(size_t)s * Hq + g * G + row] = lv;
-        }
+    const float inv = (L > 0.f) ? 1.f / L : (L == 0.f ? 0.f : nan);
+    const float val = bad ? nan : U * inv;
+    const __bf16 bv = (__bf16)val;
+    o[((size_t)s * Hq + h) * D + dim] = __builtin_bit_cast(uint16_t, bv);
+    if (lse != nullptr && dim == 0) {
+        float lv = (M == kNegInf) ? kNegInf : (M * c + log2f(L)) * kLn2;
+        if (bad || L != L) lv = nan;
+        lse[(size_t)s * Hq + h] = lv;
     }
 }
 
@@ -346,7 +335,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        a.workspace, a.Hq, a.Hkv, a.max_blocks, a.num_blocks, nsplit, a.c, a.negate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2((unsigned)a.Hkv, (unsigned)a.S), b2(256);
+    const dim3 g2((unsigned)a.Hq, (unsigned)a.S), b2(D);
     hipLaunchKernelGGL((decode_combine_kernel<D>), g2, b2, 0, stream, a.workspace, a.ctx_lens,
                        static_cast<uint16_t*>(a.o), a.lse, a.S, a.Hq, a.Hkv, a.max_blocks, nsplit, a.c);
     return hipGetLastError();
