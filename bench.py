@@ -181,11 +181,13 @@ def main(argv=None):
     dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
 
-    # decode with the 256 MB last-level cache flushed before every call
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # decode with the 256 MB last-level cache flushed before every call: a
+    # read-only sweep of 1 GiB (a write sweep would leave dirty lines whose
+    # write-back the timed call would pay for)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     fl_ms = []
     for _ in range(max(5, K // 5)):
-        flush.fill_(1)
+        flush.amax()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         decode()
@@ -250,7 +252,7 @@ def main(argv=None):
                    "bytes": db, "flops": decode_flops(p, dcfg),
                    "flushed_avg_us": round(fl_avg * 1e3, 2),
                    "flushed_GBps": round(db / (fl_avg * 1e-3) / 1e9, 1),
-                   "kernels": "decode_partial_kernel<128> + decode_combine_kernel<128>",
+                   "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
                    "traffic": profiled_traffic("paged_decode_bf16_d128_s64",
                                                ["decode_paged.hip", "common.h", "internal.h"])},
         "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,

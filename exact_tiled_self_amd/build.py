@@ -31,7 +31,12 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 # Per-source additions.  The bf16 prefill never produces or consumes a NaN
 # (masked scores are -inf), so maxima need no NaN canonicalisation.
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {
+    "prefill_bf16.hip": ["-fno-honor-nans"],
+    # matrix-core accumulators in ordinary VGPRs: the decode loop rescales
+    # them every block, which in AGPRs costs a read and a write per element
+    "decode_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:

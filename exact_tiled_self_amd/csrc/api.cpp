@@ -134,8 +134,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, int block_size) {
     if (S < 1 || Hq < 1 || d < 1 || max_blocks < 1 || block_size != attn::kDecodeBlock) return 0;
-    const size_t nsplit = (size_t)attn::decode_num_splits(max_blocks);
-    return (size_t)S * Hq * nsplit * (size_t)(d + 2) * sizeof(float);
+    return attn::decode_workspace_bound(S, Hq, d);
 }
 
 attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -158,8 +157,8 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
     if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
     if ((long long)num_blocks * Hkv * block_size * d >= (1LL << 40))
         return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
-    if ((long long)S * Hkv * attn::decode_num_splits(max_blocks) >= (1LL << 31) || S > 65535 || Hkv > 65535)
-        return fail(ATTN_ERR_UNSUPPORTED, "too many sequences or splits for one launch");
+    if ((long long)S * Hkv * max_blocks >= (1LL << 31) || S > 65535 || Hkv > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "too many sequences or blocks for one launch");
     const size_t need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);

@@ -5,34 +5,43 @@
 // rápida y fusión de operadores", section "Atención tipo FlashAttention y
 // atención paginada").  Every key position is translated through the table.
 //
-// Work split.  One workgroup per (sequence, kv head, 512-token split); each
-// of its 4 waves streams 8 consecutive logical blocks (128 tokens) in steps
-// of two blocks, with two register sets so that the loads of step j+1 are in
-// flight while step j computes, and keeps its own running state (m, l, u).
-// The G query heads that share the kv head (grouped-query attention) form
-// the rows of the score tile, so the two products are genuine small matrix
-// products and run on MFMA (v_mfma_f32_16x16x32_bf16, G <= 16 rows):
-//   * S^T = K Q^T: the lane's A operand is 8 dims of one key, loaded straight
-//     from the block; each lane ends up owning one query row (lane % 16) and
-//     4 keys of each block.
-//   * O^T = V^T P^T: P^T comes from the lane's own score registers (keys
-//     4g..4g+3 of both blocks); the V^T operand needs 8 keys of one dim per
-//     lane, so each lane loads 16-byte row slices of its 8 keys (coalesced:
-//     16 lanes cover one 256-byte row) and transposes the 8x8 block in
-//     registers with v_perm.  The output again has one query row per lane,
-//     so the rescale by e^(m - m') is lane-local.
-// The four waves' states are merged in LDS by the rescale rule of the online
-// softmax, and the workgroup writes one fp32 partial state per query head to
-// the workspace.  A second kernel merges the partial states of a sequence in
-// split order (deterministic): M = max m_k, L = sum l_k e^(m_k - M),
+// Work split.  The units of a call are the (sequence, kv head, block)
+// triples, ordered by sequence, then kv head, then block.  A fixed number of
+// waves W (4 independent waves per workgroup) each take one contiguous range
+// of floor(U / W) or ceil(U / W) units, so every wave streams the same number
+// of bytes whatever the mix of lengths, and no wave waits on another.  Each
+// wave first sums the block counts of all sequences (a wave-wide scan of the
+// lengths) to find where its range starts.  A wave's range crosses into at
+// most a few (sequence, kv head) pairs; for each piece it runs the online
+// softmax over its blocks and then either writes the final output (it
+// covered the whole pair) or leaves an fp32 partial state (m, l, u) per
+// query head in the workspace.  A second kernel merges the partial states of
+// a pair in wave order (deterministic): M = max m_k, L = sum l_k e^(m_k - M),
 // O = sum u_k e^(m_k - M) / L ("FlashAttention" notes, section "No basta con
 // promediar los resultados de los bloques": each part enters with its own
 // weight, not as an average).
 //
-// Slots past a sequence's length inside its last block are loaded (they are
-// inside the block) but their V rows are zeroed and their scores excluded
-// before any arithmetic, so stale or NaN contents cannot leak in.  Table
-// entries past the length are never read.
+// Inside a piece the wave keeps four register buffers of one block each
+// (K and V, 8 KB at d = 128): the loads of the next three blocks are in
+// flight while one block computes.  Every load goes through a buffer
+// resource sized to the block's valid rows, so slots past the sequence's
+// length and blocks with an out-of-range table entry read as zeros without
+// a branch; scores of such slots are excluded before any arithmetic.  The G
+// query heads that share the kv head (grouped-query attention) form the rows
+// of the score tile, so both products run on MFMA:
+//   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (l16, grp) holds key l16's
+//     dims D/4*grp .. D/4*grp + D/4 - 1 (one contiguous run per lane; Q uses
+//     the same dim order), and gets back the scores of keys 4grp..4grp+3 for
+//     query row l16.
+//   * O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, one tile per 16 output
+//     dims): the P^T operand is exactly the lane's four scores; the V^T
+//     operand wants 4 keys of one dim, so each lane loads D/16 consecutive
+//     dims of keys 4grp..4grp+3 (4 whole rows per load instruction) and
+//     packs key pairs with v_perm; tile j holds dims D/16*m + j.  The output
+//     comes back as one query row per lane with D/4 consecutive dims, so the
+//     rescale by e^(m - m') is lane-local.
+
+#include <stdlib.h>
 
 #include "common.h"
 #include "internal.h"
@@ -40,11 +49,8 @@
 namespace attn {
 namespace {
 
-constexpr int DC_THREADS = 256;
-constexpr int DC_WAVE_BLOCKS = 8;        // 128 tokens per wave
-constexpr int DC_STEP_BLOCKS = 2;        // 32 tokens per pipeline step
-constexpr int DC_STEPS = DC_WAVE_BLOCKS / DC_STEP_BLOCKS;
-static_assert(4 * DC_WAVE_BLOCKS * kDecodeBlock == kDecodeSplit, "split = 4 waves x 8 blocks");
+constexpr int DS_THREADS = 256;   // 4 independent waves
+constexpr int DS_NBUF = 4;        // one block computing, three in flight
 
 template <int D>
 struct VRow;
@@ -53,291 +59,407 @@ struct VRow<128> { typedef u32x4 T; };
 template <>
 struct VRow<64> { typedef u32x2 T; };
 
-// Registers of one pipeline step (two blocks): K operands and V row slices.
 template <int D>
-struct StepRegs {
-    u32x4 k[DC_STEP_BLOCKS][D / 32];
-    typename VRow<D>::T v[8];
-    int phys[DC_STEP_BLOCKS];
-    bool valid[DC_STEP_BLOCKS];
+__device__ __forceinline__ typename VRow<D>::T buf_ld_vrow(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ u32x4 buf_ld_vrow<128>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return buf_ld16(r, off);
+}
+template <>
+__device__ __forceinline__ u32x2 buf_ld_vrow<64>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// K operands and V row slices of one 16-token block.
+template <int D>
+struct KVBuf {
+    u32x4 k[D / 32];
+    typename VRow<D>::T v[4];
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int nblocks_of(int ctx, int cap) {
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    return (ctx + kDecodeBlock - 1) / kDecodeBlock;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// With U units dealt to W waves as [floor(wU/W), floor((w+1)U/W)), the wave
+// that covers unit u.
+__device__ __forceinline__ int wave_of_unit(long long u, long long U, int W) {
+    return (int)(((u + 1) * (long long)W - 1) / U);
+}
+
 template <int D>
-__global__ void __launch_bounds__(DC_THREADS)
-decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                      const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
-                      const int32_t* __restrict__ ctx_lens, float* __restrict__ ws, int Hq,
-                      int Hkv, int max_blocks, int num_blocks, int nsplit, float c, int negate) {
-    constexpr int KS = D / 32;              // MFMA k-steps over the head dim
-    constexpr int DPL = D / 16;             // dims per lane column of an MFMA
-    using VT = typename VRow<D>::T;
+__global__ void __launch_bounds__(DS_THREADS)
+decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
+                    const int32_t* __restrict__ ctx_lens, int32_t* __restrict__ recs,
+                    float* __restrict__ slots, uint16_t* __restrict__ o, float* __restrict__ lse,
+                    int S, int Hq, int Hkv, int max_blocks, int num_blocks, float c, int negate) {
+    constexpr int KS = D / 32;     // MFMA k-steps over the head dim
+    constexpr int DPL = D / 16;    // output tiles; V dims per lane per key
+    constexpr int QW = D / 4;      // dims per lane group in the score product
+    constexpr int NB = DS_NBUF, LA = DS_NBUF - 1;
 
-    __shared__ float sm_m[4][16];
-    __shared__ float sm_l[4][16];
-    __shared__ __attribute__((aligned(16))) float sm_o[4][16][D];
+    const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+    const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = Hq / Hkv, cap = max_blocks * kDecodeBlock;
+    const int mlp = decode_ml_pad(G);
+    const size_t sf = decode_slot_floats(G, D);
 
-    const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-    const int G = Hq / Hkv;
-    const int cap = max_blocks * kDecodeBlock;
-    int ctx = ctx_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);     // out-of-range lengths: see combine
-    const int nsplit_s = (ctx + kDecodeSplit - 1) / kDecodeSplit;
-    if (split >= nsplit_s) return;
+    // Total block count over the sequences.
+    int n_first = 0, tot = 0;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int n = (s0 + lane < S) ? nblocks_of(ctx_lens[s0 + lane], cap) : 0;
+        if (s0 == 0) n_first = n;
+        tot += wave_sum_i(n);
+    }
+    tot = __builtin_amdgcn_readfirstlane(tot);
+    // Units are dealt to W = min(waves launched, U) waves, so that every
+    // wave in [0, W) has at least one unit (the merge relies on it).
+    const long long U = (long long)tot * Hkv;
+    const int W = (int)min((long long)gridDim.x * 4, U);
+    if (w >= W) return;
+    const long long u0 = (long long)w * U / W, u1 = (long long)(w + 1) * U / W;
 
-    // the wave index is uniform: keep the block-table walk in scalar registers
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, grp = lane >> 4;
-    const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
-    const int fb = split * (kDecodeSplit / kDecodeBlock) + wave * DC_WAVE_BLOCKS;
-    const int wblocks = min(max(nblk - fb, 0), DC_WAVE_BLOCKS);
-    const int nsteps = (wblocks + DC_STEP_BLOCKS - 1) / DC_STEP_BLOCKS;
-
-    // The wave's table entries, fetched once up front (lane j holds entry
-    // fb + j), so that no K/V load waits behind a table read; entries outside
-    // [0, num_blocks) are not followed (the sequence's output becomes NaN).
-    int tab = 0;
-    if (lane < wblocks) tab = table[(size_t)s * max_blocks + fb + lane];
-    const bool tab_ok = lane < wblocks && tab >= 0 && tab < num_blocks;
-    const uint64_t valid_mask = __builtin_amdgcn_ballot_w64(tab_ok);
-    const bool bad = __builtin_amdgcn_ballot_w64(lane < wblocks && !tab_ok) != 0;
-
-    // Q operand (B of S^T = K Q^T): query row l16 (head g*G + l16 when l16 < G),
-    // dims 8*(4ks + grp) .. +7.
-    bf16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (l16 < G) w = ld16(q + ((size_t)s * Hq + g * G + l16) * D + 8 * (4 * ks + grp));
-        if (negate) w = neg_bf16x8(w);
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
+    // The sequence holding unit u0 (unit of (s, g, b) = Hkv*P_s + g*n_s + b,
+    // P_s = blocks of the sequences before s).
+    int s = 0, Ps = 0, ns = 0;
+    {
+        int P = 0;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const int n = (s0 == 0) ? n_first : ((s0 + lane < S) ? nblocks_of(ctx_lens[s0 + lane], cap) : 0);
+            const int incl = wave_incl_scan(n, lane);
+            const long long lo = (long long)Hkv * (P + incl - n), hi = (long long)Hkv * (P + incl);
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(u0 >= lo && u0 < hi);
+            if (hit) {
+                const int j = (int)__builtin_ctzll(hit);
+                const int nj = __builtin_amdgcn_readlane(n, j);
+                s = s0 + j;
+                Ps = P + __builtin_amdgcn_readlane(incl, j) - nj;
+                ns = nj;
+                break;
+            }
+            P += __builtin_amdgcn_readlane(incl, 63);
+        }
     }
 
-    auto load_step = [&](StepRegs<D>& R, int st) {
+    const float nanv = __builtin_nanf("");
+    long long u = u0;
+    while (true) {
+        // ---- one piece: blocks [b0, b1) of pair (s, g) ----
+        const long long base = (long long)Hkv * Ps;
+        const int r0 = (int)(u - base);
+        const int g = r0 / ns, b0 = r0 - g * ns;
+        const long long pbeg = base + (long long)g * ns, pend = pbeg + ns;
+        const long long send = pend < u1 ? pend : u1;
+        const int b1 = b0 + (int)(send - u), nb = b1 - b0;
+        const int p = s * Hkv + g;
+        const int ctx_raw = ctx_lens[s];
+        const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
+        const bool ctx_bad = ctx_raw < 0 || ctx_raw > cap;
+
+        // Q operand (B of S^T = K Q^T): query row l16 (head g*G + l16 when l16 < G).
+        bf16x8 qf[KS];
 #pragma unroll
-        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
-            const int j = st * DC_STEP_BLOCKS + bi;            // block index within the wave
-            const bool ok = (valid_mask >> j) & 1;
-            R.phys[bi] = ok ? __builtin_amdgcn_readlane(tab, j) : 0;
-            R.valid[bi] = ok;
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 wq = {0u, 0u, 0u, 0u};
+            if (l16 < G) wq = ld16(q + ((size_t)s * Hq + g * G + l16) * D + QW * grp + 8 * ks);
+            if (negate) wq = neg_bf16x8(wq);
+            qf[ks] = __builtin_bit_cast(bf16x8, wq);
         }
+
+        // Per-lane byte offsets inside a block: K row l16, dims QW*grp..;
+        // V rows 4grp..4grp+3, dims DPL*l16...
+        const uint32_t ul = threadIdx.x & 63u;
+        const uint32_t koff = (ul & 15u) * (uint32_t)(D * 2) + (ul >> 4) * (uint32_t)(QW * 2);
+        const uint32_t voff = (ul >> 4) * (uint32_t)(4 * D * 2) + (ul & 15u) * (uint32_t)(DPL * 2);
+        const int32_t* trow = table + (size_t)s * max_blocks + b0;
+        bool bad = false;
+        int tab = 0;     // table entries of the current chunk (lane j: block cb + j)
+
+        auto issue = [&](KVBuf<D>& R, int i, int cb, int cn) {
+            int bytes = 0;
+            size_t off = 0;
+            if (i < cn) {
+                const int e = __builtin_amdgcn_readlane(tab, i);
+                const bool ok = e >= 0 && e < num_blocks;
+                bad = bad || !ok;
+                const int nv = min(kDecodeBlock, ctx - kDecodeBlock * (b0 + cb + i));
+                bytes = ok ? nv * D * 2 : 0;
+                off = ((size_t)(ok ? e : 0) * Hkv + g) * (size_t)(kDecodeBlock * D);
+            }
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + off, (uint32_t)bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + off, (uint32_t)bytes);
+            // opaque copies keep the constant parts in the instructions'
+            // offset fields instead of hoisted per-load address registers
+            uint32_t ko = koff, vo = voff;
+            asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
-        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
-            const uint16_t* kb = kc + (((size_t)R.phys[bi] * Hkv + g) * kDecodeBlock + l16) * D;
+            for (int ks = 0; ks < KS; ++ks) R.k[ks] = buf_ld16(rk, ko + (uint32_t)(ks * 16));
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) R.v[rr] = buf_ld_vrow<D>(rv, vo + (uint32_t)(rr * D * 2));
+        };
+
+        // Running state (m, l, u) of the online softmax for this piece.
+        float m_run = kNegInf, l_run = 0.f;
+        f32x4 oacc[DPL];
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key0 = 4 * grp;
+
+        auto compute = [&](KVBuf<D>& R, int i, int cb) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                R.k[bi][ks] = R.valid[bi] ? ld16(kb + 8 * (4 * ks + grp)) : u32x4{0u, 0u, 0u, 0u};
-        }
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.k[ks]), qf[ks], sc, 0, 0, 0);
+            // lane: query row l16, keys key0 + rr of the block
+            const int nv = min(kDecodeBlock, ctx - kDecodeBlock * (b0 + cb + i));
+            float mx = kNegInf;
+            bool ok[4];
 #pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-            const int bi = i8 >> 2;
-            const uint16_t* vr = vc + (((size_t)R.phys[bi] * Hkv + g) * kDecodeBlock + 4 * grp + (i8 & 3)) * D;
-            R.v[i8] = R.valid[bi] ? *reinterpret_cast<const VT*>(vr + DPL * l16) : VT{};
-        }
-    };
-
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 oacc[DPL];
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute_step = [&](StepRegs<D>& R, int st) {
-        const int tok0 = (fb + st * DC_STEP_BLOCKS) * kDecodeBlock;
-        f32x4 sacc[DC_STEP_BLOCKS];
-#pragma unroll
-        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi) {
-            sacc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.k[bi][ks]),
-                                                                   qf[ks], sacc[bi], 0, 0, 0);
-        }
-        // lane: query row l16, keys 4*grp + r of each block
-        float mx = kNegInf;
-#pragma unroll
-        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = R.valid[bi] && (tok0 + bi * kDecodeBlock + 4 * grp + r) < ctx;
-                sacc[bi][r] = ok ? sacc[bi][r] : kNegInf;
-                mx = fmaxf(mx, sacc[bi][r]);
+            for (int rr = 0; rr < 4; ++rr) {
+                ok[rr] = key0 < nv - rr;
+                mx = fmaxf(mx, ok[rr] ? sc[rr] : kNegInf);
             }
-        mx = fmaxf(mx, xor_shfl(mx, 16));
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_use) * c);
-        const float mc = m_use * c;
-        float lsum = 0.f;
+            mx = fmaxf(mx, xor_shfl(mx, 16));
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            m_run = m_new;
+            const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+            float ps = 0.f;
+            s16x4 pb;
 #pragma unroll
-        for (int bi = 0; bi < DC_STEP_BLOCKS; ++bi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sv = sacc[bi][r];
-                const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
-                sacc[bi][r] = p;
-                lsum += p;
+            for (int rr = 0; rr < 4; ++rr) {
+                const float pv = ok[rr] ? fast_exp2(fmaf(sc[rr], c, -mc)) : 0.f;
+                ps += pv;
+                pb[rr] = __builtin_bit_cast(short, (__bf16)pv);
             }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-        // P^T operand: row l16, keys (4grp..4grp+3) of block 0 then of block 1
-        bf16x8 pb;
+            l_run = fmaf(l_run, alpha, ps);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pb[i] = (__bf16)sacc[0][i];
-            pb[4 + i] = (__bf16)sacc[1][i];
-        }
-        // V rows of positions past the length are zeroed (NaN-safe)
-#pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8)
-            if (!(R.valid[i8 >> 2] && (tok0 + (i8 >> 2) * kDecodeBlock + 4 * grp + (i8 & 3)) < ctx))
-                R.v[i8] = VT{};
-        // O^T += V^T P^T: A operand = 8 keys of dim DPL*l16 + j (8x8 register transpose)
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-            const int w = j >> 1;
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 t;
-            t.x = __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], sel);
-            t.y = __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], sel);
-            t.z = __builtin_amdgcn_perm(R.v[5][w], R.v[4][w], sel);
-            t.w = __builtin_amdgcn_perm(R.v[7][w], R.v[6][w], sel);
-            oacc[j] *= alpha;
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t), pb,
-                                                              oacc[j], 0, 0, 0);
-        }
-    };
+            for (int j = 0; j < DPL; ++j) {
+                const int wd = j >> 1;
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                u32x2 a2;
+                a2.x = __builtin_amdgcn_perm(R.v[1][wd], R.v[0][wd], sel);
+                a2.y = __builtin_amdgcn_perm(R.v[3][wd], R.v[2][wd], sel);
+                oacc[j] *= alpha;
+                oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a2), pb,
+                                                                    oacc[j], 0, 0, 0);
+            }
+        };
 
-    // Two register sets, ping-pong: the loads of step st+1 are in flight
-    // while step st computes.
-    StepRegs<D> ra, rb;
-    if (nsteps > 0) load_step(ra, 0);
+        // Chunks of up to 64 blocks (one table entry per lane).  Within a
+        // chunk: NB blocks per trip, each trip issuing the loads LA blocks
+        // ahead (past the chunk they are empty); then the last < NB blocks,
+        // whose loads are in flight already.
+        KVBuf<D> bufs[NB];
 #pragma unroll 1
-    for (int st = 0; st < nsteps; st += 2) {
-        if (st + 1 < nsteps) load_step(rb, st + 1);
-        compute_step(ra, st);
-        if (st + 1 < nsteps) {
-            if (st + 2 < nsteps) load_step(ra, st + 2);
-            compute_step(rb, st + 1);
+        for (int cb = 0; cb < nb; cb += 64) {
+            const int cn = min(64, nb - cb);
+            tab = (lane < cn) ? trow[cb + lane] : 0;
+#pragma unroll
+            for (int k = 0; k < LA; ++k) issue(bufs[k], k, cb, cn);
+            int i = 0;
+#pragma unroll 1
+            for (; i + NB <= cn; i += NB) {
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    issue(bufs[(k + LA) % NB], i + k + LA, cb, cn);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(bufs[k], i + k, cb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < LA; ++k)
+                if (i + k < cn) compute(bufs[k], i + k, cb);
         }
-    }
 
-    // lane: row l16, dims DPL*(4grp + r) + j.  Merge the four waves in LDS.
-    l_run += xor_shfl(l_run, 16);
-    l_run += xor_shfl(l_run, 32);
-    if (grp == 0) {
-        sm_m[wave][l16] = m_run;
-        sm_l[wave][l16] = bad ? __builtin_nanf("") : l_run;
-    }
-    if (l16 < G) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) sm_o[wave][l16][DPL * (4 * grp + r) + j] = oacc[j][r];
-    }
-    __syncthreads();
-
-    float* part = ws + ((size_t)(s * Hkv + g) * nsplit + split) * (size_t)G * (D + 2);
-    for (int e = tid; e < G * D; e += DC_THREADS) {
-        const int row = e / D, dim = e - row * D;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][row]);
-        float U = 0.f, Lw = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = sm_m[w][row];
-            const float f = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * c);
-            U = fmaf(f, sm_o[w][row][dim], U);
-            Lw = fmaf(f, sm_l[w][row], Lw);
+        // ---- write the piece ----
+        l_run += xor_shfl(l_run, 16);
+        l_run += xor_shfl(l_run, 32);
+        if (b0 == 0 && lane == 0) {
+            recs[2 * p] = w;                                   // first wave of the pair
+            recs[2 * p + 1] = wave_of_unit(pend - 1, U, W);    // last wave of the pair
         }
-        part[2 * G + e] = U;
-        if (dim == 0) {
-            part[row] = M;
-            part[G + row] = Lw;
+        if (b0 == 0 && b1 == ns) {
+            // the whole pair: final output
+            const bool nan_out = bad || ctx_bad;
+            const float inv = nan_out ? nanv : 1.f / l_run;
+            if (l16 < G) {
+                uint16_t* orow = o + ((size_t)s * Hq + g * G + l16) * D + QW * grp;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if constexpr (DPL == 8) {
+                        u32x4 pk;
+                        pk.x = pack_bf16x2(oacc[0][rr] * inv, oacc[1][rr] * inv);
+                        pk.y = pack_bf16x2(oacc[2][rr] * inv, oacc[3][rr] * inv);
+                        pk.z = pack_bf16x2(oacc[4][rr] * inv, oacc[5][rr] * inv);
+                        pk.w = pack_bf16x2(oacc[6][rr] * inv, oacc[7][rr] * inv);
+                        st16(orow + DPL * rr, pk);
+                    } else {
+                        u32x2 pk;
+                        pk.x = pack_bf16x2(oacc[0][rr] * inv, oacc[1][rr] * inv);
+                        pk.y = pack_bf16x2(oacc[2][rr] * inv, oacc[3][rr] * inv);
+                        *reinterpret_cast<u32x2*>(orow + DPL * rr) = pk;
+                    }
+                }
+                if (lse != nullptr && grp == 0)
+                    lse[(size_t)s * Hq + g * G + l16] = nan_out ? nanv : (m_run * c + log2f(l_run)) * kLn2;
+            }
+        } else {
+            float* slot = slots + (size_t)(w + p) * sf;
+            if (l16 < G) {
+                if (grp == 0) {
+                    slot[l16] = m_run;
+                    slot[G + l16] = bad ? nanv : l_run;
+                }
+                float* ud = slot + mlp + (size_t)l16 * D + QW * grp;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                    for (int j4 = 0; j4 < DPL; j4 += 4)
+                        *reinterpret_cast<f32x4*>(ud + DPL * rr + j4) =
+                            f32x4{oacc[j4][rr], oacc[j4 + 1][rr], oacc[j4 + 2][rr], oacc[j4 + 3][rr]};
+            }
+        }
+
+        // ---- next piece ----
+        u = send;
+        if (u >= u1) break;
+        if (g + 1 == Hkv) {
+            Ps += ns;
+            do {
+                ++s;
+                ns = nblocks_of(ctx_lens[s], cap);
+            } while (ns == 0);
         }
     }
 }
 
-// One workgroup per (query head, sequence), one thread per output dim:
-// merge the sequence's split states for that head in split order (fixed
-// order, so the result is deterministic):  M = max m_k,
-// L = sum l_k e^(m_k - M), O = sum u_k e^(m_k - M) / L, lse = M + ln L.
-// Each wave reads the splits' (m_k, l_k) with one load per lane (split k in
-// lane k), reduces them across lanes, and then issues all the u_k loads of
-// its dim at once.
+// Merge: one wave per (pair, 64 (row, 4-dim) elements).  Each lane walks
+// the partial states that the waves wf..wl left for the pair, in wave order
+// (deterministic), sixteen at a time with all their loads issued together,
+// and keeps a running merged state: when a part's m exceeds the running
+// maximum the running l and u are rescaled first, so every part enters with
+// the weight e^(m_k - M).  Pairs covered by one wave were finished by that
+// wave; empty sequences give o = 0 and lse = -inf (NaN for a length outside
+// [0, max_blocks * 16]).
 template <int D>
-__global__ void __launch_bounds__(D)
-decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ ctx_lens,
-                      uint16_t* __restrict__ o, float* __restrict__ lse, int S, int Hq, int Hkv,
-                      int max_blocks, int nsplit, float c) {
-    const int h = blockIdx.x, s = blockIdx.y, dim = threadIdx.x, lane = dim & 63;
-    const int G = Hq / Hkv, g = h / G, row = h - g * G;
+__global__ void __launch_bounds__(64)
+decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ slots,
+                    const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ o,
+                    float* __restrict__ lse, int Hq, int Hkv, int max_blocks, float c) {
+    constexpr int NQ = D / 4;     // 4-dim groups per row
+    constexpr int BATCH = 16;
+    const int p = blockIdx.x, lane = threadIdx.x;
+    const int s = p / Hkv, g = p - s * Hkv, G = Hq / Hkv;
+    const int e = blockIdx.y * 64 + lane;          // element: row e / NQ, dims 4*(e % NQ)..
+    const int row = e / NQ, d4 = e - row * NQ;
+    const bool act = row < G;
     const int cap = max_blocks * kDecodeBlock;
-    int ctx = ctx_lens[s];
-    const bool bad = ctx < 0 || ctx > cap;
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    const int nsp = (ctx + kDecodeSplit - 1) / kDecodeSplit;
-    const size_t stride = (size_t)G * (D + 2);
-    const float* base = ws + (size_t)(s * Hkv + g) * nsplit * stride;
-
-    // M over all splits, 64 per pass
-    float M = kNegInf;
-    for (int k0 = 0; k0 < nsp; k0 += 64) {
-        const float mk = (k0 + lane < nsp) ? base[(k0 + lane) * stride + row] : kNegInf;
-        float mx = mk;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        M = fmaxf(M, mx);
+    // the record is read before the length check so both loads are in flight together
+    const int wf = recs[2 * p], wl = recs[2 * p + 1];
+    const int ctx_raw = ctx_lens[s];
+    const bool bad = ctx_raw < 0 || ctx_raw > cap;
+    const float nanv = __builtin_nanf("");
+    uint16_t* orow = o + ((size_t)s * Hq + g * G + row) * D + 4 * d4;
+    float* lse_out = (lse != nullptr && act && d4 == 0) ? lse + (size_t)s * Hq + g * G + row : nullptr;
+    if (nblocks_of(ctx_raw, cap) == 0) {
+        if (act) {
+            const uint32_t z = bad ? 0x7fc07fc0u : 0u;
+            *reinterpret_cast<u32x2*>(orow) = u32x2{z, z};
+        }
+        if (lse_out) *lse_out = bad ? nanv : kNegInf;
+        return;
     }
-    float L = 0.f, U = 0.f;
-    for (int k0 = 0; k0 < nsp; k0 += 64) {
-        const bool in = k0 + lane < nsp;
-        const float mk = in ? base[(k0 + lane) * stride + row] : kNegInf;
-        const float lk = in ? base[(k0 + lane) * stride + G + row] : 0.f;
-        const float fk = (mk == kNegInf) ? 0.f : fast_exp2((mk - M) * c);
-        float lw = fk * lk;
+    if (wf == wl || !act) return;
+    const int nk = wl - wf + 1;
+    const size_t sf = decode_slot_floats(G, D);
+    const int mlp = decode_ml_pad(G);
+    const float* s0 = slots + (size_t)(wf + p) * sf;
+
+    float M = kNegInf, L = 0.f;
+    f32x4 U = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nk; k0 += BATCH) {
+        float mk[BATCH], lk[BATCH];
+        f32x4 uk[BATCH];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off, 64);
-        L += lw;
-        const int nk = min(64, nsp - k0);
-        // u loads in groups of 16, all issued before they are summed (in split order)
-        for (int j0 = 0; j0 < nk; j0 += 16) {
-            float uv[16], fw[16];
+        for (int j = 0; j < BATCH; ++j) {
+            const int k = min(k0 + j, nk - 1);
+            const float* sl = s0 + (size_t)k * sf;
+            mk[j] = sl[row];
+            lk[j] = sl[G + row];
+            uk[j] = *reinterpret_cast<const f32x4*>(sl + mlp + (size_t)row * D + 4 * d4);
+        }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int kk = min(j0 + j, nk - 1);
-                fw[j] = (j0 + j < nk) ? __shfl(fk, kk, 64) : 0.f;
-                uv[j] = base[(k0 + kk) * stride + 2 * G + row * D + dim];
+        for (int j = 0; j < BATCH; ++j) {
+            if (k0 + j < nk && mk[j] > M) {
+                const float r = (M == kNegInf) ? 0.f : fast_exp2((M - mk[j]) * c);
+                L *= r;
+                U *= r;
+                M = mk[j];
             }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) U = fmaf(fw[j], uv[j], U);
+            const float f = (k0 + j >= nk || mk[j] == kNegInf) ? 0.f : fast_exp2((mk[j] - M) * c);
+            L = fmaf(f, lk[j], L);
+            U += f * uk[j];
         }
     }
-    const float nan = __builtin_nanf("");
-    const float inv = (L > 0.f) ? 1.f / L : (L == 0.f ? 0.f : nan);
-    const float val = bad ? nan : U * inv;
-    const __bf16 bv = (__bf16)val;
-    o[((size_t)s * Hq + h) * D + dim] = __builtin_bit_cast(uint16_t, bv);
-    if (lse != nullptr && dim == 0) {
+    const float inv = bad ? nanv : (L > 0.f ? 1.f / L : (L == 0.f ? 0.f : nanv));
+    u32x2 pk;
+    pk.x = pack_bf16x2(U.x * inv, U.y * inv);
+    pk.y = pack_bf16x2(U.z * inv, U.w * inv);
+    *reinterpret_cast<u32x2*>(orow) = pk;
+    if (lse_out) {
         float lv = (M == kNegInf) ? kNegInf : (M * c + log2f(L)) * kLn2;
-        if (bad || L != L) lv = nan;
-        lse[(size_t)s * Hq + h] = lv;
+        if (bad || L != L) lv = nanv;
+        *lse_out = lv;
     }
 }
 
 template <int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    const int nsplit = decode_num_splits(a.max_blocks);
-    const dim3 g1((unsigned)nsplit, (unsigned)a.Hkv, (unsigned)a.S), b1(DC_THREADS);
-    hipLaunchKernelGGL((decode_partial_kernel<D>), g1, b1, 0, stream,
+    // ATTN_DECODE_WAVES (4..2048, a multiple of 4) lowers the wave count so
+    // that tests can reach long pieces, many pieces per wave and wide merges
+    // with small inputs.
+    int waves = kDecodeWaves;
+    if (const char* env = getenv("ATTN_DECODE_WAVES")) {
+        const int v = atoi(env);
+        if (v >= 4 && v <= kDecodeWaves) waves = v / 4 * 4;
+    }
+    const long long units_max = (long long)a.S * a.Hkv * a.max_blocks;
+    if (units_max < waves) waves = (int)((units_max + 3) / 4 * 4);
+    int32_t* recs = reinterpret_cast<int32_t*>(a.workspace);
+    float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + decode_rec_bytes(a.S, a.Hkv));
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(waves / 4)), dim3(DS_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
-                       static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens,
-                       a.workspace, a.Hq, a.Hkv, a.max_blocks, a.num_blocks, nsplit, a.c, a.negate);
+                       static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, recs, slots,
+                       static_cast<uint16_t*>(a.o), a.lse, a.S, a.Hq, a.Hkv, a.max_blocks, a.num_blocks,
+                       a.c, a.negate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2((unsigned)a.Hq, (unsigned)a.S), b2(D);
-    hipLaunchKernelGGL((decode_combine_kernel<D>), g2, b2, 0, stream, a.workspace, a.ctx_lens,
-                       static_cast<uint16_t*>(a.o), a.lse, a.S, a.Hq, a.Hkv, a.max_blocks, nsplit, a.c);
+    const int elems = (a.Hq / a.Hkv) * (D / 4);
+    const dim3 g2((unsigned)(a.S * a.Hkv), (unsigned)((elems + 63) / 64));
+    hipLaunchKernelGGL((decode_merge_kernel<D>), g2, dim3(64), 0, stream, recs, slots, a.ctx_lens,
+                       static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.max_blocks, a.c);
     return hipGetLastError();
 }
 

@@ -24,11 +24,29 @@ struct PrefillArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
-// Paged decode: keys are processed in splits of kDecodeSplit tokens, each
-// producing an fp32 partial state (m, l, u) per query head in the workspace,
-// which a second kernel merges.
-constexpr int kDecodeSplit = 512;
+// Paged decode: the (sequence, kv head, 16-token block) units of a call are
+// dealt out to a fixed number of waves in equal contiguous ranges; a wave
+// whose range covers only part of a (sequence, kv head) pair leaves an fp32
+// partial state (m, l, u) per query head in the workspace, which a second
+// kernel merges.
 constexpr int kDecodeBlock = 16;   // tokens per KV-cache block
+constexpr int kDecodeWaves = 2048; // waves of the split kernel (8 per CU on 256 CUs)
+
+// Workspace layout: per-pair records (first and last wave of the pair, two
+// int32 each) padded to 256 bytes, then one slot per (wave, pair) touch
+// (at most kDecodeWaves + S*Hkv of them) of [m[G], l[G], pad to 4, u[G][d]].
+inline size_t decode_rec_bytes(int S, int Hkv) {
+    return (((size_t)S * Hkv * 2 * sizeof(int32_t)) + 255) & ~(size_t)255;
+}
+__host__ __device__ inline int decode_ml_pad(int G) { return (2 * G + 3) & ~3; }
+__host__ __device__ inline size_t decode_slot_floats(int G, int d) { return (size_t)decode_ml_pad(G) + (size_t)G * d; }
+// Upper bound over every Hkv dividing Hq (the size query does not take Hkv).
+inline size_t decode_workspace_bound(int S, int Hq, int d) {
+    const size_t rec = (((size_t)S * Hq * 2 * sizeof(int32_t)) + 255) & ~(size_t)255;
+    const size_t slots_times_g = (size_t)kDecodeWaves * Hq + (size_t)S * Hq;   // >= (W + S*Hkv) * G
+    const size_t slots = (size_t)kDecodeWaves + (size_t)S * Hq;                // >= W + S*Hkv
+    return rec + (slots_times_g * (size_t)(d + 2) + slots * 3) * sizeof(float);
+}
 
 struct DecodeArgs {
     const void* q;
@@ -43,10 +61,6 @@ struct DecodeArgs {
     int negate;
     float* workspace;
 };
-
-inline int decode_num_splits(int max_blocks) {
-    return (int)(((long long)max_blocks * kDecodeBlock + kDecodeSplit - 1) / kDecodeSplit);
-}
 
 hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 

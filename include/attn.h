@@ -91,7 +91,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 /*
  * attn_paged_decode_workspace_size - bytes of device workspace that
  * attn_paged_decode needs for these sizes (0 on invalid sizes).  The
- * workspace holds the fp32 partial states (m, l, u) of the key splits.
+ * workspace holds, per (sequence, kv head) pair, the first and last wave that
+ * worked on it, and the fp32 partial states (m, l, u) that waves covering
+ * only part of a pair leave for the merge.  The size is a bound that holds
+ * for every Hkv dividing Hq: round_up(8*S*Hq, 256)
+ * + 4*((2048 + S)*Hq*(d + 2) + 3*(2048 + S*Hq)) bytes.
  */
 size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, int block_size);
 

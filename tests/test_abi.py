@@ -104,9 +104,14 @@ def test_decode_rejects_before_any_launch(lib, kw, status):
 
 
 def test_workspace_size(lib):
-    # fp32 partial state (m, l, u[d]) per query head and 512-token split
-    assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == 64 * 12 * 16 * 130 * 4
-    assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 16) == 1 * 1 * 1 * 66 * 4
+    # documented bound: 8*S*Hq bytes of pair records rounded up to 256, then
+    # fp32 partial states for up to 2048 + S*Hq wave pieces
+    def expect(S, Hq, d):
+        rec = (8 * S * Hq + 255) // 256 * 256
+        return rec + 4 * ((2048 + S) * Hq * (d + 2) + 3 * (2048 + S * Hq))
+    assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == expect(64, 12, 128)
+    assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 16) == expect(1, 1, 64)
+    assert lib.attn_paged_decode_workspace_size(3, 8, 64, 7, 16) == expect(3, 8, 64)
     assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 32) == 0
     assert lib.attn_paged_decode_workspace_size(0, 1, 64, 1, 16) == 0
 

@@ -1,9 +1,12 @@
 """GPU parity of attn_paged_decode against the float64 oracle: the full
 64-sequence workload, ragged lengths, NaN poison in every slot that must not
 be read, a spike key located through the block table, an identity table
-against dense attention, empty contexts and determinism."""
+against dense attention, empty contexts, bad device-resident lengths and
+table entries, many sequences, the wave count forced down (long pieces,
+several pieces per wave, wide merges) and determinism."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -153,3 +156,53 @@ def test_full_workload_and_determinism():
     o1, l1 = run_decode(p, PAGED_CONFIG.scale)
     o2, l2 = run_decode(p, PAGED_CONFIG.scale)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("waves", [4, 12, 36, 2048])
+def test_wave_counts(monkeypatch, waves):
+    """Few waves give long pieces (several 64-block table chunks), waves that
+    cross many (sequence, kv head) pairs, and pairs merged from many waves."""
+    rng = np.random.default_rng(41)
+    ctx = rng.integers(0, 3000, 70)
+    ctx[[3, 10, 11, 50]] = 0
+    ctx[5] = 4096
+    p = paged_inputs(small_cfg(), S=70, ctx_lens=ctx.tolist(), poison=True, extra_blocks=4,
+                     max_blocks=256, seed=42)
+    monkeypatch.setenv("ATTN_DECODE_WAVES", str(waves))
+    o, lse = run_decode(p, 0.0884)
+    check(p, 0.0884, f"waves={waves}")
+    o2, lse2 = run_decode(p, 0.0884)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_many_short_sequences():
+    rng = np.random.default_rng(43)
+    ctx = rng.integers(0, 40, 200)
+    p = paged_inputs(small_cfg(Hq=8, Hkv=2, d=64), S=200, ctx_lens=ctx.tolist(), poison=True,
+                     max_blocks=3, seed=44)
+    check(p, 0.125, "S=200 short")
+
+
+@pytest.mark.parametrize("waves", [4, 2048])
+def test_bad_device_inputs_give_nan(monkeypatch, waves):
+    """Lengths outside [0, max_blocks*16] and needed table entries outside
+    [0, num_blocks) make that sequence's outputs NaN, touch nothing out of
+    bounds, and leave the other sequences exact."""
+    ctx = [100, 300, 200, 50, 700, 33]
+    p = paged_inputs(small_cfg(), S=6, ctx_lens=ctx, poison=True, max_blocks=48, seed=45)
+    ref_o, ref_l = oracle_decode(p, 0.0884)
+    cap = 48 * 16
+    p["ctx_lens"] = p["ctx_lens"].clone()
+    p["ctx_lens"][1] = -3
+    p["ctx_lens"][3] = cap + 5
+    p["block_table"] = p["block_table"].clone()
+    p["block_table"][4, 20] = p["num_blocks"]       # inside sequence 4's 44 blocks
+    p["block_table"][5, 1] = -7                      # inside sequence 5's 3 blocks
+    monkeypatch.setenv("ATTN_DECODE_WAVES", str(waves))
+    o, lse = run_decode(p, 0.0884)
+    for s in (1, 3, 4, 5):
+        assert torch.isnan(o[s].float()).all(), s
+        assert torch.isnan(lse[s]).all(), s
+    for s in (0, 2):
+        assert max_abs(f64(o[s]), ref_o[s]) <= O_TOL[torch.bfloat16]
+        assert max_abs(lse[s].double().numpy(), ref_l[s]) <= LSE_TOL
