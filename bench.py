@@ -85,7 +85,7 @@ def profiled_traffic(profile: str, sources) -> float | None:
     return traffic if digest == h.hexdigest()[:16] else None
 
 
-def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=5):
+def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100):
     """The fp64 oracle, as it stands, on the prefill workload's host copy.
 
     The whole workload fits in a few seconds of host time, so the sample is
