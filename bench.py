@@ -105,10 +105,23 @@ def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100):
                       f"T={cfg.N}, d={cfg.d}, causal), float64 numpy oracle on the host copy"}
 
 
+def read_clocks():
+    """sclk / mclk lines of `rocm-smi --showclocks` (run as a child process right
+    after the timed loop), or None when the tool is unavailable."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=20).stdout
+    except Exception:
+        return None
+    lines = [ln.strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln]
+    return lines[:4] or None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
@@ -186,7 +199,7 @@ def main(argv=None):
     # write-back the timed call would pay for)
     flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     fl_ms = []
-    for _ in range(max(5, K // 5)):
+    for _ in range(max(20, K // 2)):
         flush.amax()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -209,6 +222,8 @@ def main(argv=None):
                              p["v_cache"].float().numpy(), p["block_table"].numpy()[sub],
                              p["ctx_lens"].numpy()[sub], 16, dcfg.scale)
     derr = float(np.abs(od[torch.as_tensor(sub)].double().cpu().numpy() - ro).max())
+
+    clocks = read_clocks()
 
     pf = prefill_flops(pcfg)
     pre_avg = float(np.mean(pre_ms))
@@ -246,11 +261,14 @@ def main(argv=None):
                      "algorithmic_bytes": prefill_bytes(pcfg),
                      "kernel": "prefill_bf16_kernel<128, causal>",
                      "per_launch": {"flops": pf, "avg_us": round(pre_avg * 1e3, 2),
+                                    "median_us": round(float(np.median(pre_ms)) * 1e3, 2),
                                     "min_us": round(min(pre_ms) * 1e3, 2)}},
         "decode": {"value": round(gbps, 1), "unit": "GB/s", "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
-                   "avg_us": round(dec_avg * 1e3, 2), "min_us": round(min(dec_ms) * 1e3, 2),
+                   "avg_us": round(dec_avg * 1e3, 2), "median_us": round(float(np.median(dec_ms)) * 1e3, 2),
+                   "min_us": round(min(dec_ms) * 1e3, 2),
                    "bytes": db, "flops": decode_flops(p, dcfg),
                    "flushed_avg_us": round(fl_avg * 1e3, 2),
+                   "flushed_median_us": round(float(np.median(fl_ms)) * 1e3, 2),
                    "flushed_GBps": round(db / (fl_avg * 1e-3) / 1e9, 1),
                    "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
                    "traffic": profiled_traffic("paged_decode_bf16_d128_s64",
@@ -258,6 +276,7 @@ def main(argv=None):
         "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,
                    "tolerance": 2e-2},
         "wall_s_timed": round(wall, 3),
+        "clocks_after_timing": clocks,
         "library": _lib.library_path(),
     }
     if not args.no_cpu_baseline:
