@@ -209,6 +209,20 @@ def main(argv=None):
         fl_ms.append(e0.elapsed_time(e1))
     del flush
 
+    # the decode step replayed from a HIP graph of 8 calls (no per-call launch)
+    from exact_tiled_self_amd.graph import DecodeGraph
+    dg = DecodeGraph(pd["q"], pd["k_cache"], pd["v_cache"], pd["block_table"], pd["ctx_lens"], 16,
+                     dcfg.scale, calls=8)
+    g_ms = []
+    for _ in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        g_ms.append(e0.elapsed_time(e1) / 8)
+    del dg
+
     # parity spot check on the benchmarked buffers (sampled rows / sequences)
     from oracle import exact as OA
     rows = np.array([0, 1, 4095, 8190, 8191])
@@ -270,6 +284,7 @@ def main(argv=None):
                    "flushed_avg_us": round(fl_avg * 1e3, 2),
                    "flushed_median_us": round(float(np.median(fl_ms)) * 1e3, 2),
                    "flushed_GBps": round(db / (fl_avg * 1e-3) / 1e9, 1),
+                   "graph_replay_median_us": round(float(np.median(g_ms)) * 1e3, 2),
                    "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
                    "traffic": profiled_traffic("paged_decode_bf16_d128_s64",
                                                ["decode_paged.hip", "common.h", "internal.h"])},

@@ -206,3 +206,47 @@ def test_bad_device_inputs_give_nan(monkeypatch, waves):
     for s in (0, 2):
         assert max_abs(f64(o[s]), ref_o[s]) <= O_TOL[torch.bfloat16]
         assert max_abs(lse[s].double().numpy(), ref_l[s]) <= LSE_TOL
+
+
+def test_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph: replayed several times, with
+    eager library calls in between and the inputs rewritten in place between
+    replays (new queries, one more token per sequence written into its block),
+    every replay equals an eager call on the same buffers bit for bit."""
+    from exact_tiled_self_amd.graph import DecodeGraph
+    rng = np.random.default_rng(71)
+    ctx = rng.integers(100, 3000, 16)
+    p = paged_inputs(small_cfg(), S=16, ctx_lens=ctx.tolist(), extra_blocks=40, max_blocks=200, seed=72)
+    d = _dev(p)
+    # free pool blocks (never referenced) to grow into
+    used = set(p["block_table"].numpy()[p["block_table"].numpy() >= 0].tolist())
+    free = [b for b in range(p["num_blocks"]) if b not in used]
+    g = DecodeGraph(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["ctx_lens"], 16, 0.0884,
+                    calls=2)
+    for rep in range(4):
+        o_g, l_g = g.replay()
+        torch.cuda.synchronize()
+        o_e, l_e = attn_paged_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                     d["ctx_lens"], 16, 0.0884)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), rep
+        # next step: new queries, and one more token appended to every sequence
+        d["q"].copy_(torch.randn(d["q"].shape, generator=torch.Generator().manual_seed(rep)).to(d["q"]))
+        lens = d["ctx_lens"].cpu()
+        table = d["block_table"].cpu()
+        for s in range(16):
+            pos = int(lens[s])
+            if pos % 16 == 0:
+                table[s, pos // 16] = free.pop()
+            blk = int(table[s, pos // 16])
+            d["k_cache"][blk, :, pos % 16] = torch.randn(2, 128, generator=torch.Generator().manual_seed(s)).to(d["k_cache"])
+            d["v_cache"][blk, :, pos % 16] = torch.randn(2, 128, generator=torch.Generator().manual_seed(99 + s)).to(d["v_cache"])
+        d["block_table"].copy_(table)
+        d["ctx_lens"].copy_(lens + 1)
+    # the final state against the oracle
+    o_g, l_g = g.replay()
+    torch.cuda.synchronize()
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ro, rl = oracle_decode(host, 0.0884)
+    assert max_abs(f64(o_g), ro) <= O_TOL[torch.bfloat16]
+    assert max_abs(l_g.cpu().double().numpy(), rl) <= LSE_TOL
