@@ -13,6 +13,8 @@ recurrence  a scalar model of the block-by-block online-softmax recurrence
             (running max m, sum l, numerator u, rescale by e^(m - m')), the
             merge of two such states, and the naive block average the pages
             warn against
+kvcache     appending new tokens' keys and values to a paged KV cache,
+            one token at a time through the block table
 
 Sources (web pages; cited by title and section):
   [AT]  "Autoatención, kernels CUDA y FlashAttention", section 1 (how
@@ -36,3 +38,4 @@ from .recurrence import (  # noqa: F401
     merge_states,
     naive_block_average,
 )
+from .kvcache import append_paged  # noqa: F401
