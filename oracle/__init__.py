@@ -8,7 +8,8 @@ or links it, and this package imports nothing from the product path.
 Modules
 -------
 exact       the plain definition, softmax(s * Q K^T) V per head, with every
-            score row materialised in float64 (dense prefill and paged decode)
+            score row materialised in float64 (dense prefill, paged decode and
+            chunked prefill over a paged cache)
 recurrence  a scalar model of the block-by-block online-softmax recurrence
             (running max m, sum l, numerator u, rescale by e^(m - m')), the
             merge of two such states, and the naive block average the pages
@@ -31,7 +32,7 @@ invariants, a library routine on float64 CPU tensors and 40-digit brute force
 on tiny inputs.  No function is parity-unpinned.
 """
 
-from .exact import attention, attention_rows, paged_decode, gather_paged_kv  # noqa: F401
+from .exact import attention, attention_rows, paged_decode, paged_prefill, gather_paged_kv  # noqa: F401
 from .recurrence import (  # noqa: F401
     OnlineState,
     online_aggregate,

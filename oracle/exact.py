@@ -33,6 +33,11 @@ notes):
             "Atención tipo FlashAttention y atención paginada"); the single
             decode query attends to all ctx_lens[s] positions; an empty
             context gives o = 0 and lse = -inf.
+  * chunked the new query rows of all sequences are packed: q, o [T, Hq, d],
+            lse [T, Hq]; rows starts[s] .. starts[s+1]-1 belong to sequence
+            s, whose ctx_lens[s] positions already include them, so its
+            t-th new row sits at position ctx_lens[s] - n_s + t and attends
+            to positions 0 .. that one (causal, diagonal included).
 """
 
 from __future__ import annotations
@@ -43,7 +48,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["sigma_of", "kv_head_of", "attention", "attention_rows",
-           "gather_paged_kv", "paged_decode", "default_workers"]
+           "gather_paged_kv", "paged_decode", "paged_prefill", "default_workers"]
 
 
 def sigma_of(scale: float) -> float:
@@ -196,5 +201,61 @@ def paged_decode(q, k_cache, v_cache, block_table, ctx_lens, block_size, scale,
         lse[s, heads] = lb
 
     items = [(s, g) for s in range(S) for g in range(Hkv)]
+    _run_items(work, items, default_workers() if workers is None else workers)
+    return o, lse
+
+
+def paged_prefill(q, k_cache, v_cache, block_table, ctx_lens, starts, block_size, scale,
+                  *, workers=None):
+    """Chunked prefill over a paged KV cache, the plain definition.
+
+    q: [T, Hq, d] packed new rows; k_cache, v_cache: [num_blocks, Hkv,
+    block_size, d]; block_table: int [S, max_blocks]; ctx_lens: int [S]
+    (lengths including the new rows); starts: int [S + 1].
+    Returns (o [T, Hq, d], lse [T, Hq]) as float64.  Row t of sequence s is
+    query position ctx_lens[s] - n_s + t, which sees keys 0 .. that position
+    gathered through the table.  Rows that belong to no sequence are NaN.
+
+    The library's contract for inputs it cannot check before launch is
+    modelled too: a sequence with ctx_lens[s] < n_s or ctx_lens[s] >
+    max_blocks * block_size gets NaN rows, and so does every row whose keys
+    include a block with a table entry outside [0, num_blocks).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, d = q.shape
+    kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+    num_blocks, Hkv = kc.shape[0], kc.shape[1]
+    table = np.asarray(block_table)
+    max_blocks = table.shape[1]
+    ctx_lens, starts = np.asarray(ctx_lens), np.asarray(starts)
+    S = table.shape[0]
+    sigma = sigma_of(scale)
+    o = np.full((T, Hq, d), np.nan)
+    lse = np.full((T, Hq), np.nan)
+
+    def work(item):
+        s, g = item
+        a, b = int(starts[s]), int(starts[s + 1])
+        n, ctx = b - a, int(ctx_lens[s])
+        if n <= 0 or ctx < n or ctx > max_blocks * block_size:
+            return
+        first = ctx - n
+        pos = first + np.arange(n)
+        entries = table[s, :(ctx + block_size - 1) // block_size]
+        bad = np.nonzero((entries < 0) | (entries >= num_blocks))[0]
+        ok = pos < (bad[0] * block_size if len(bad) else ctx)   # rows that read only good blocks
+        if not ok.any():
+            return
+        nk = int(pos[ok].max()) + 1
+        kk, vv = gather_paged_kv(kc, vc, table, nk, s, g, block_size)
+        heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
+        rows = np.nonzero(ok)[0]
+        for h in heads:
+            ob, lb = _complete_rows(q[a + rows, h], kk, vv, sigma, pos[rows], True)
+            o[a + rows, h] = ob
+            lse[a + rows, h] = lb
+
+    items = [(s, g) for s in range(S) for g in range(Hkv)
+             if 0 <= int(starts[s]) <= int(starts[s + 1]) <= T]
     _run_items(work, items, default_workers() if workers is None else workers)
     return o, lse
