@@ -7,7 +7,7 @@ library; the first call does, and raises if it is missing.
 """
 
 __all__ = ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-           "AttnError", "library_path", "abi_version"]
+           "attn_kv_append", "attn_paged_prefill", "AttnError", "library_path", "abi_version"]
 
 
 def __getattr__(name):

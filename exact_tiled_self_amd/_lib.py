@@ -19,7 +19,7 @@ import torch
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-           "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
+           "attn_kv_append", "attn_paged_prefill", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_BF16"]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_NO_DEVICE, ATTN_ERR_LAUNCH = range(5)
@@ -61,6 +61,12 @@ def raw_library():
         lib.attn_paged_decode.restype = ci
         lib.attn_paged_decode.argtypes = [vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci,
                                           cf, ci, vp, sz, vp]
+        lib.attn_kv_append.restype = ci
+        lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
+                                       ci, vp]
+        lib.attn_paged_prefill.restype = ci
+        lib.attn_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci,
+                                           ci, ci, ci, cf, ci, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ci]
         lib.attn_last_error.restype = ctypes.c_char_p
@@ -162,5 +168,64 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, ctx_lens, block_size=16,
         _dev(o, "o"), _dev(lse, "lse") if lse is not None else None, S, Hq, Hkv, d, max_blocks,
         num_blocks, float(scale), _DTYPE[q.dtype], _dev(workspace, "workspace"), ws_bytes,
         _stream_ptr(q.device, stream))
+    _check(st)
+    return o, lse
+
+
+def _paged_meta(k_cache, v_cache, block_table, ctx_lens, starts, block_size):
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("the caches must both be [num_blocks, Hkv, block_size, d] of one dtype")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32 or starts.dtype != torch.int32:
+        raise ValueError("block_table, ctx_lens and starts must be int32")
+    S = ctx_lens.shape[0]
+    if ctx_lens.dim() != 1 or block_table.dim() != 2 or block_table.shape[0] != S \
+            or tuple(starts.shape) != (S + 1,) or k_cache.shape[2] != block_size:
+        raise ValueError("inconsistent paged-cache shapes")
+    return S, k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], block_table.shape[1]
+
+
+def attn_kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_lens, starts, block_size=16, *,
+                   max_new=None, stream=None):
+    """Write packed new tokens k_new, v_new [T, Hkv, d] into the paged caches
+    in place.  starts: int32 [S + 1] row offsets; ctx_lens: int32 [S], the
+    lengths after the append.  max_new bounds every sequence's new-token
+    count and sizes the launch (default T, always safe)."""
+    S, num_blocks, Hkv, d, max_blocks = _paged_meta(k_cache, v_cache, block_table, ctx_lens, starts,
+                                                    block_size)
+    if k_new.dim() != 3 or v_new.shape != k_new.shape or tuple(k_new.shape[1:]) != (Hkv, d):
+        raise ValueError("k_new and v_new must be [T, Hkv, d] matching the caches")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or k_cache.dtype not in _DTYPE:
+        raise ValueError("new rows and caches must share dtype float32 or bfloat16")
+    T = k_new.shape[0]
+    st = raw_library().attn_kv_append(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(ctx_lens, "ctx_lens"), _dev(starts, "starts"),
+        int(block_size), S, T, T if max_new is None else int(max_new), Hkv, d, max_blocks, num_blocks,
+        _DTYPE[k_cache.dtype], _stream_ptr(k_cache.device, stream))
+    _check(st)
+
+
+def attn_paged_prefill(q, k_cache, v_cache, block_table, ctx_lens, starts, block_size=16, scale=None,
+                       *, max_new=None, o=None, lse=None, want_lse=True, stream=None):
+    """Chunked prefill of packed query rows q [T, Hq, d] against the paged
+    cache (their own keys already appended): returns (o [T, Hq, d], lse
+    [T, Hq]).  Rows of no sequence are left as allocated."""
+    S, num_blocks, Hkv, d, max_blocks = _paged_meta(k_cache, v_cache, block_table, ctx_lens, starts,
+                                                    block_size)
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_cache.dtype or q.dtype not in _DTYPE:
+        raise ValueError("q must be [T, Hq, d] with the caches' d and dtype")
+    T, Hq = q.shape[0], q.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = raw_library().attn_paged_prefill(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(ctx_lens, "ctx_lens"), _dev(starts, "starts"),
+        int(block_size), _dev(o, "o"), _dev(lse, "lse") if lse is not None else None, S, T,
+        T if max_new is None else int(max_new), Hq, Hkv, d, max_blocks, num_blocks, float(scale),
+        _DTYPE[q.dtype], _stream_ptr(q.device, stream))
     _check(st)
     return o, lse

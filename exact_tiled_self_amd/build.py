@@ -22,17 +22,20 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "prefill_paged.hip",
+           "kv_append.hip"]
 
 # Device-code flags: gfx950 only; packed fp32 instructions disabled.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 
-# Per-source additions.  The bf16 prefill never produces or consumes a NaN
-# (masked scores are -inf), so maxima need no NaN canonicalisation.
+# Per-source additions.  The bf16 prefill kernels never produce or consume a
+# NaN in arithmetic (masked scores are -inf; the paged one writes its NaN
+# results as bit patterns), so maxima need no NaN canonicalisation.
 EXTRA_FLAGS = {
     "prefill_bf16.hip": ["-fno-honor-nans"],
+    "prefill_paged.hip": ["-fno-honor-nans"],
     # matrix-core accumulators in ordinary VGPRs: the decode loop rescales
     # them every block, which in AGPRs costs a read and a write per element
     "decode_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -192,4 +192,103 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
     return launch_status(attn::launch_paged_decode_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens, const int32_t* starts,
+                           int block_size, int S, int T, int max_new, int Hkv, int d, int max_blocks,
+                           int num_blocks, attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !ctx_lens || !starts)
+        return fail(ATTN_ERR_INVALID_ARG, "k_new, v_new, k_cache, v_cache, block_table, ctx_lens and starts must be non-null");
+    if (S < 1 || Hkv < 1 || d < 1 || max_blocks < 1 || num_blocks < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "S, Hkv, d, max_blocks and num_blocks must be >= 1");
+    if (T < 0 || max_new < 0) return fail(ATTN_ERR_INVALID_ARG, "T and max_new must be >= 0");
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const size_t es = elem_size(dtype);
+    const size_t row = (size_t)d * es;
+    if (row % 16 != 0 || row > 4096)
+        return fail(ATTN_ERR_UNSUPPORTED, "d * element size must be a multiple of 16 bytes, at most 4096");
+    if (block_size < 1 || block_size > 1024)
+        return fail(ATTN_ERR_UNSUPPORTED, "block_size %d is not supported (1 .. 1024)", block_size);
+    if (S > 65535) return fail(ATTN_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+    if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
+    const int cpr = (int)(row / 16);
+    if ((long long)max_new * Hkv * cpr >= (1LL << 31) - 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "max_new too large for one launch");
+    if ((long long)num_blocks * Hkv * block_size * (long long)row >= (1LL << 48))
+        return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(starts, 4))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, ctx_lens and starts must be 4-byte aligned");
+    const size_t nb = (size_t)T * Hkv * row, cb = (size_t)num_blocks * Hkv * block_size * row;
+    const void* ins[5] = {k_new, v_new, block_table, ctx_lens, starts};
+    const size_t insz[5] = {nb, nb, (size_t)S * max_blocks * 4, (size_t)S * 4, (size_t)(S + 1) * 4};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(k_cache, cb, ins[i], insz[i]) || overlap(v_cache, cb, ins[i], insz[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "the caches must not overlap the inputs");
+    if (overlap(k_cache, cb, v_cache, cb)) return fail(ATTN_ERR_INVALID_ARG, "k_cache and v_cache must not overlap");
+    if (T == 0 || max_new == 0) return ATTN_OK;
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+
+    attn::KvAppendArgs a;
+    a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.block_table = block_table; a.ctx_lens = ctx_lens; a.starts = starts;
+    a.S = S; a.T = T; a.max_new = max_new; a.Hkv = Hkv; a.block_size = block_size;
+    a.max_blocks = max_blocks; a.num_blocks = num_blocks; a.cpr = cpr;
+    return launch_status(attn::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_lens, const int32_t* starts,
+                               int block_size, void* o, float* lse, int S, int T, int max_new, int Hq,
+                               int Hkv, int d, int max_blocks, int num_blocks, float scale,
+                               attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !starts || !o)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, ctx_lens, starts and o must be non-null");
+    if (S < 1 || Hq < 1 || Hkv < 1 || max_blocks < 1 || num_blocks < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "S, Hq, Hkv, max_blocks and num_blocks must be >= 1");
+    if (T < 0 || max_new < 0) return fail(ATTN_ERR_INVALID_ARG, "T and max_new must be >= 0");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged prefill supports bf16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
+    if (block_size != attn::kDecodeBlock)
+        return fail(ATTN_ERR_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
+    if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
+    if ((long long)max_new * Hq * d * 2 >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "max_new * Hq * d * 2 must be below 2^31");
+    if ((long long)((max_new + 127) / 128) * S * Hq >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    if ((long long)num_blocks * Hkv * block_size * d >= (1LL << 40))
+        return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(starts, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, ctx_lens, starts and lse must be 4-byte aligned");
+    const size_t qb = (size_t)T * Hq * d * 2, cb = (size_t)num_blocks * Hkv * block_size * d * 2;
+    const size_t lsb = lse ? (size_t)T * Hq * 4 : 0;
+    const void* ins[6] = {q, k_cache, v_cache, block_table, ctx_lens, starts};
+    const size_t insz[6] = {qb, cb, cb, (size_t)S * max_blocks * 4, (size_t)S * 4, (size_t)(S + 1) * 4};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(o, qb, ins[i], insz[i]) || overlap(lse, lsb, ins[i], insz[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "outputs must not overlap the inputs");
+    if (overlap(o, qb, lse, lsb)) return fail(ATTN_ERR_INVALID_ARG, "o and lse must not overlap");
+    if (T == 0 || max_new == 0) return ATTN_OK;
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+
+    attn::PagedPrefillArgs a;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
+    a.ctx_lens = ctx_lens; a.starts = starts; a.o = o; a.lse = lse;
+    a.S = S; a.T = T; a.max_new = max_new; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.max_blocks = max_blocks; a.num_blocks = num_blocks;
+    a.c = (float)(fabs((double)scale) * 1.4426950408889634);
+    a.negate = scale < 0.f ? 1 : 0;
+    return launch_status(attn::launch_paged_prefill_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -64,4 +64,36 @@ struct DecodeArgs {
 
 hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Packed new tokens [T, Hkv, d] written into the paged cache.
+struct KvAppendArgs {
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    const int32_t* starts;
+    int S, T, max_new, Hkv, block_size, max_blocks, num_blocks;
+    int cpr;           // 16-byte chunks per (token, kv head) row
+};
+
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+
+// Chunked prefill: packed new query rows [T, Hq, d] against the paged cache.
+struct PagedPrefillArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    const int32_t* starts;
+    void* o;
+    float* lse;        // may be null
+    int S, T, max_new, Hq, Hkv, d, max_blocks, num_blocks;
+    float c;
+    int negate;
+};
+
+hipError_t launch_paged_prefill_bf16(const PagedPrefillArgs& a, hipStream_t stream);
+
 }  // namespace attn

@@ -1,0 +1,234 @@
+// Chunked prefill over a paged KV cache, bf16 in / bf16 out, fp32
+// accumulation, for gfx950.
+//
+// The new query rows of several sequences arrive packed ([T, Hq, d]); the
+// rows of sequence s are starts[s] .. starts[s+1]-1, and since their keys and
+// values are already in the cache, its t-th new row sits at position
+// ctx_lens[s] - n_s + t and attends to every cached position up to its own
+// (causal, diagonal included).  Positions are translated through the block
+// table into the pool of 16-token blocks ("Kernels de atención rápida y
+// fusión de operadores", section "Atención tipo FlashAttention y atención
+// paginada").  One 16-token block per wave per key tile keeps each load's
+// physical block uniform across the wave, so both K and V go through one
+// buffer resource per wave and tile, sized to the block's valid rows: slots
+// past the sequence's length, and blocks whose table entry is outside the
+// pool, read as zeros with no branch.
+//
+// Everything else is the dense kernel's tile recurrence (prefill_tile.h):
+// 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in
+// LDS, K loaded straight into LDS, V stored transposed, MFMA 32x32x16 bf16
+// on S^T = K Q^T and O^T += V^T P^T, lazy rescale of the running maximum.
+// The work units are (query tile, sequence, query head), later query tiles
+// first (they see the most keys), heads fastest so the heads that share a
+// kv head run side by side and share its tiles in L2.
+//
+// Device-resident values are checked before they form an address: a
+// sequence with malformed row offsets (or more than max_new rows) is left
+// unwritten; one whose length is below its row count or beyond the table
+// gets NaN rows; a row that attends to a block with an out-of-range table
+// entry gets NaN.
+
+#include "internal.h"
+#include "prefill_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr uint32_t kNaNBf16x2 = 0x7FC07FC0u;   // two quiet bf16 NaNs
+constexpr uint32_t kNaN32 = 0x7FC00000u;       // quiet fp32 NaN
+
+template <int D>
+__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                     const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
+                     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ starts,
+                     uint16_t* __restrict__ o, float* __restrict__ lse, int S, int T, int max_new,
+                     int Hq, int Hkv, int max_blocks, int num_blocks, int n_qtiles, float c,
+                     int negate) {
+    using L = PfLayout<D>;
+    constexpr int BS = kDecodeBlock;
+    static_assert(PF_BN == PF_WAVES * BS, "one cache block per wave per key tile");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
+    __shared__ int bad_s[PF_WAVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, l32 = lane & 31;
+
+    // Work unit: (q tile, sequence, head), latest q tiles first.
+    const int SH = S * Hq;
+    const int wg = blockIdx.x;
+    const int qt = n_qtiles - 1 - wg / SH;
+    const int sh = wg - (wg / SH) * SH;
+    const int s = sh / Hq, h = sh - s * Hq;
+    const int g = h / (Hq / Hkv);
+
+    const int a = starts[s], b = starts[s + 1], ctx = ctx_lens[s];
+    const int n = b - a;
+    if (a < 0 || b > T || n < 0 || n > max_new) return;     // not this call's rows
+    const int q0 = qt * PF_BM;
+    if (q0 >= n) return;
+    const int row_end = min(q0 + PF_BM, n);
+    const int wrow0 = q0 + wave * 32;
+    const int myrow = wrow0 + l32;                            // row within the sequence
+    const size_t orow = ((size_t)(a + myrow) * Hq + h);       // row index into o / lse
+
+    if (ctx < n || ctx > max_blocks * BS) {                   // impossible length: NaN rows
+        if (hi == 0 && myrow < row_end) {
+            const u32x4 nan4 = {kNaNBf16x2, kNaNBf16x2, kNaNBf16x2, kNaNBf16x2};
+#pragma unroll
+            for (int c8 = 0; c8 < D / 8; ++c8) st16(o + orow * D + c8 * 8, nan4);
+            if (lse != nullptr) reinterpret_cast<uint32_t*>(lse)[orow] = kNaN32;
+        }
+        return;
+    }
+    const int first = ctx - n;                                // position of row 0
+    const bool wave_active = wrow0 < n;
+
+    // Q rows myrow (zero past n), dims 16*ks + 8*hi .. +7.
+    const uint32_t qstride = (uint32_t)Hq * D * 2;            // bytes between rows
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(q + ((size_t)a * Hq + h) * D, (uint32_t)(n - 1) * qstride + D * 2);
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 w = buf_ld16(qrs, (uint32_t)myrow * qstride + (uint32_t)(ks * 16 + hi * 8) * 2);
+        if (negate) w = neg_bf16x8(w);
+        qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // Keys 0 .. first + row_end - 1 are needed.
+    const int n_kt = (first + row_end - 1) / PF_BN + 1;
+
+    // This wave stages cache block kt*4 + wave of every tile: K chunk p =
+    // (wave * KINST + i) * 64 + lane of the tile (row p / CPR, a row of this
+    // block), V keys 16*wave + VKPT*kq .. + VKPT-1, dims 8*vdc .. +7.
+    uint32_t koff[L::KINST];
+#pragma unroll
+    for (int i = 0; i < L::KINST; ++i) {
+        const int p = (wave * L::KINST + i) * 64 + lane;
+        const int r = p / L::CPR;
+        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
+        koff[i] = (uint32_t)((r - wave * BS) * D + cc * 8) * 2;
+    }
+    constexpr int KGRP = BS / L::VKPT;                       // key groups per block
+    const int kq = lane % KGRP, vdc = lane / KGRP;
+    const uint32_t voff = (uint32_t)(kq * L::VKPT * D + vdc * 8) * 2;
+    const int vpos = swap23(wave * BS + kq * L::VKPT);
+    u32x4 vreg[L::VKPT];
+    const size_t head_elems = (size_t)BS * D;                 // one (block, kv head) tile
+    const int32_t* trow = table + (size_t)s * max_blocks;
+    int bad = 0x7fffffff;                                     // lowest block with a bad entry
+
+    auto issue_loads = [&](int kt, int buf) {
+        const int blk = kt * PF_WAVES + wave;
+        const int valid = min(max(ctx - blk * BS, 0), BS);    // rows of this block in the sequence
+        int phys = 0;
+        bool ok = valid > 0;
+        if (ok) {
+            phys = trow[blk];
+            if (phys < 0 || phys >= num_blocks) {
+                bad = min(bad, blk);
+                phys = 0;
+                ok = false;
+            }
+        }
+        const size_t base = ((size_t)phys * Hkv + g) * head_elems;
+        // (wave-uniform; readfirstlane keeps the resource in scalar registers)
+        const uint32_t bytes = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)valid * D * 2 : 0u);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + base, bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + base, bytes);
+        uint16_t* Ks = smem + buf * L::BUF;
+#pragma unroll
+        for (int i = 0; i < L::KINST; ++i)
+            buf_ld16_lds(krs, Ks + (wave * L::KINST + i) * 64 * 8, koff[i]);
+#pragma unroll
+        for (int i = 0; i < L::VKPT; ++i) vreg[i] = buf_ld16(vrs, voff + (uint32_t)(i * D * 2));
+    };
+    auto store_v = [&](int buf) { pf_store_vt<D>(smem + buf * L::BUF + L::KELEMS, vreg, vpos, vdc); };
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+    const int mypos = first + myrow;
+    const int wpos0 = first + wrow0;
+
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    store_v(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < n_kt;
+        if (more) issue_loads(kt + 1, buf ^ 1);
+        const int k0 = kt * PF_BN;
+        if (wave_active && k0 <= wpos0 + 31) {
+            const uint16_t* Ks = smem + buf * L::BUF;
+            const bool need_mask = k0 + PF_BN - 1 > wpos0;
+            pf_tile_step<D, true>(Ks, Ks + L::KELEMS, qf, oacc, m_run, l_run, k0, ctx, mypos,
+                                  need_mask, c, hi, l32);
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);     // tile kt+1: K in LDS, V in registers
+            store_v(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    // Lowest bad block seen by any wave of the workgroup.
+    if (lane == 0) bad_s[wave] = bad;
+    __syncthreads();
+    int bad_all = bad_s[0];
+#pragma unroll
+    for (int w = 1; w < PF_WAVES; ++w) bad_all = min(bad_all, bad_s[w]);
+
+    // Epilogue: o = u / l, lse = m + ln l (natural log); NaN for a row that
+    // attends to a block with a bad table entry.
+    const float l_tot = l_run + xor_shfl(l_run, 32);
+    if (myrow < row_end) {
+        // (NaN is written as a bit pattern: the arithmetic is compiled on
+        // the assumption that it never meets a NaN)
+        const bool poisoned = bad_all != 0x7fffffff && bad_all * BS <= mypos;
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        uint16_t* op = o + orow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int dim0 = db * 32 + rg * 8 + hi * 4;
+                u32x2 w = {pack_bf16x2(oacc[db][rg * 4 + 0] * inv, oacc[db][rg * 4 + 1] * inv),
+                           pack_bf16x2(oacc[db][rg * 4 + 2] * inv, oacc[db][rg * 4 + 3] * inv)};
+                if (poisoned) w = u32x2{kNaNBf16x2, kNaNBf16x2};
+                *reinterpret_cast<u32x2*>(op + dim0) = w;
+            }
+        if (lse != nullptr && hi == 0) {
+            const float lv = (m_run * c + log2f(l_tot)) * kLn2;
+            reinterpret_cast<uint32_t*>(lse)[orow] = poisoned ? kNaN32 : __builtin_bit_cast(uint32_t, lv);
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_paged_prefill_t(const PagedPrefillArgs& a, hipStream_t stream) {
+    const int n_qt = (a.max_new + PF_BM - 1) / PF_BM;
+    const dim3 grid((unsigned)(n_qt * a.S * a.Hq)), block(PF_THREADS);
+    hipLaunchKernelGGL((prefill_paged_kernel<D>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
+                       static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, a.starts,
+                       static_cast<uint16_t*>(a.o), a.lse, a.S, a.T, a.max_new, a.Hq, a.Hkv,
+                       a.max_blocks, a.num_blocks, n_qt, a.c, a.negate);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill_bf16(const PagedPrefillArgs& a, hipStream_t stream) {
+    return a.d == 128 ? launch_paged_prefill_t<128>(a, stream) : launch_paged_prefill_t<64>(a, stream);
+}
+
+}  // namespace attn

@@ -13,6 +13,9 @@ Workloads (shapes from the pages' examples):
     ("FlashAttention" notes, last section; "Kernels de atención rápida...",
     section "Atención tipo FlashAttention y atención paginada").
   * paged-KV decode with 16-token blocks (same section of the last page).
+  * chunked prefill over that paged cache: each sequence brings a chunk of
+    new rows whose keys and values are appended to the cache and whose
+    queries attend to everything cached up to their own position.
 
 Recipe: numpy.random.default_rng(seed).standard_normal(shape, float32) drawn
 in the order q, k, v (after the context lengths and the block permutation
@@ -30,8 +33,8 @@ from dataclasses import dataclass, asdict
 import numpy as np
 import torch
 
-__all__ = ["DenseConfig", "PagedConfig", "DENSE_CONFIGS", "PAGED_CONFIG",
-           "dense_inputs", "paged_inputs", "torch_dtype"]
+__all__ = ["DenseConfig", "PagedConfig", "DENSE_CONFIGS", "PAGED_CONFIG", "CHUNK_NEW",
+           "dense_inputs", "paged_inputs", "chunked_inputs", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -87,6 +90,10 @@ DENSE_CONFIGS = {
 
 PAGED_CONFIG = PagedConfig("paged_decode_s64", S=64, Hq=12, Hkv=2, d=128, block_size=16,
                            ctx_lo=512, ctx_hi=8192, max_blocks=512, dtype="bf16", seed=4)
+
+
+# New rows per sequence in the chunked-prefill workload over PAGED_CONFIG's cache.
+CHUNK_NEW = 256
 
 
 def torch_dtype(name: str):
@@ -172,3 +179,33 @@ def paged_inputs(cfg: PagedConfig = PAGED_CONFIG, *, S=None, ctx_lens=None, seed
     return dict(q=_cast(q, cfg.dtype), k_cache=_cast(kc, cfg.dtype), v_cache=_cast(vc, cfg.dtype),
                 block_table=torch.from_numpy(table), ctx_lens=torch.from_numpy(ctx),
                 num_blocks=num_blocks, max_blocks=max_blocks, block_size=bs)
+
+
+def chunked_inputs(cfg: PagedConfig = PAGED_CONFIG, *, new_lens, S=None, ctx_lens=None, seed=None,
+                   poison=False, extra_blocks=0, max_blocks=None):
+    """A paged cache (as paged_inputs) plus a packed chunk of new rows.
+
+    new_lens: the number of new rows of every sequence (an int for all, or
+    one per sequence); each must not exceed that sequence's length, which
+    counts them.  Adds to paged_inputs' dict: q_new [T,Hq,d], k_new and
+    v_new [T,Hkv,d] (cfg dtype), starts int32 [S+1] (row offsets), new_lens
+    int32 [S] and max_new.  The new rows are drawn from
+    default_rng(seed + 1) in the order q_new, k_new, v_new, after the cache.
+    """
+    seed = cfg.seed if seed is None else seed
+    p = paged_inputs(cfg, S=S, ctx_lens=ctx_lens, seed=seed, poison=poison,
+                     extra_blocks=extra_blocks, max_blocks=max_blocks)
+    ctx = p["ctx_lens"].numpy().astype(np.int64)
+    n = np.broadcast_to(np.asarray(new_lens, dtype=np.int64), ctx.shape).copy()
+    if (n < 0).any() or (n > ctx).any():
+        raise ValueError("every new_lens entry must lie in [0, ctx_lens]")
+    starts = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    T = int(starts[-1])
+    rng = np.random.default_rng(seed + 1)
+    qn = rng.standard_normal((T, cfg.Hq, cfg.d), dtype=np.float32)
+    kn = rng.standard_normal((T, cfg.Hkv, cfg.d), dtype=np.float32)
+    vn = rng.standard_normal((T, cfg.Hkv, cfg.d), dtype=np.float32)
+    p.update(q_new=_cast(qn, cfg.dtype), k_new=_cast(kn, cfg.dtype), v_new=_cast(vn, cfg.dtype),
+             starts=torch.from_numpy(starts), new_lens=torch.from_numpy(n.astype(np.int32)),
+             max_new=int(n.max(initial=0)))
+    return p

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_OK = 0,
@@ -136,6 +136,92 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
                               int d, int max_blocks, int num_blocks, float scale,
                               attn_dtype dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * attn_kv_append - write new tokens' keys and values into a paged KV cache
+ * ("Kernels de atención rápida y fusión de operadores", section "Atención
+ * tipo FlashAttention y atención paginada": the cache grows by a token, or a
+ * chunk of tokens, per step and is kept as fixed-size blocks reached through
+ * a block table).  A pure copy: the bytes land unchanged.
+ *
+ *   k_new, v_new  : [T, Hkv, d] element type `dtype`; the new tokens of all
+ *                   sequences packed row after row
+ *   starts        : int32 [S + 1]; rows starts[s] .. starts[s+1]-1 are the
+ *                   n_s new tokens of sequence s (n_s may be 0)
+ *   ctx_lens      : int32 [S]; lengths AFTER the append (they count the new
+ *                   tokens): token t of sequence s goes to position
+ *                   p = ctx_lens[s] - n_s + t, i.e. block
+ *                   block_table[s][p / block_size], slot p % block_size, for
+ *                   every kv head.  Neither lengths nor table are modified.
+ *   k_cache,
+ *   v_cache       : [num_blocks, Hkv, block_size, d] element type `dtype`,
+ *                   written in place; every other slot keeps its bytes
+ *   block_table   : int32 [S, max_blocks]
+ *   max_new       : host-side upper bound on every n_s; it sizes the launch
+ *
+ * Supported: dtype F32 or BF16; d * element size a multiple of 16 bytes and
+ * at most 4096 bytes; 1 <= block_size <= 1024; 1 <= S <= 65535; T >= 0 and
+ * max_new >= 0 (either 0: nothing to write, returns OK without a launch);
+ * Hkv, max_blocks, num_blocks >= 1.  k_new, v_new, k_cache, v_cache 16-byte
+ * aligned; block_table, ctx_lens, starts 4-byte aligned; the caches must not
+ * overlap each other or any input.
+ *
+ * Device-resident values never cause an out-of-bounds access.  A sequence
+ * whose offsets are malformed (starts[s] < 0, starts[s+1] > T or
+ * starts[s+1] < starts[s]), with n_s > max_new, or with ctx_lens[s] < n_s
+ * writes nothing; a token whose block index is >= max_blocks or whose table
+ * entry is outside [0, num_blocks) is not written.  Two new tokens that map
+ * to the same slot race (which one lands is unspecified).
+ */
+attn_status attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens,
+                           const int32_t* starts, int block_size, int S, int T, int max_new,
+                           int Hkv, int d, int max_blocks, int num_blocks, attn_dtype dtype,
+                           void* stream);
+
+/*
+ * attn_paged_prefill - chunked (variable-length) prefill against a paged KV
+ * cache: several new query rows per sequence, each attending causally to
+ * every cached position up to its own (same page and section as above; the
+ * per-row result is the attention definition at the top of this file).
+ *
+ *   q, o          : [T, Hq, d] bf16; the new query rows of all sequences
+ *                   packed row after row
+ *   lse           : fp32 [T, Hq], or NULL
+ *   starts        : int32 [S + 1]; rows starts[s] .. starts[s+1]-1 belong to
+ *                   sequence s (n_s rows, may be 0)
+ *   ctx_lens      : int32 [S]; cached length of sequence s, which already
+ *                   includes its n_s new tokens (append them first): row t of
+ *                   sequence s is position ctx_lens[s] - n_s + t and attends
+ *                   to positions 0 .. that one, diagonal included
+ *   k_cache,
+ *   v_cache       : [num_blocks, Hkv, block_size, d] bf16, as in
+ *                   attn_paged_decode
+ *   block_table   : int32 [S, max_blocks]
+ *   max_new       : host-side upper bound on every n_s; it sizes the launch
+ *
+ * With n_s = 1 for every sequence this is attn_paged_decode; with no earlier
+ * context (ctx_lens[s] = n_s) it is causal attn_fwd over each sequence.
+ * Rows that belong to no sequence are not written.
+ *
+ * Supported: dtype BF16; d = 64 or 128; block_size = 16; Hq % Hkv == 0;
+ * S, Hq, Hkv, max_blocks, num_blocks >= 1; T >= 0 and max_new >= 0 (either
+ * 0: nothing to do, returns OK without a launch); max_new * Hq * d * 2 <
+ * 2^31.  q, o, k_cache, v_cache 16-byte aligned; block_table, ctx_lens,
+ * starts, lse 4-byte aligned; o and lse must not overlap the inputs or
+ * each other.
+ *
+ * Device-resident values never cause an out-of-bounds access.  A sequence
+ * whose offsets are malformed (as for attn_kv_append) or with n_s > max_new
+ * is not written; one with ctx_lens[s] < n_s or ctx_lens[s] > max_blocks *
+ * block_size gets NaN in o and lse; a row that attends to a block whose
+ * table entry is outside [0, num_blocks) gets NaN.
+ */
+attn_status attn_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               const int32_t* starts, int block_size, void* o, float* lse, int S,
+                               int T, int max_new, int Hq, int Hkv, int d, int max_blocks,
+                               int num_blocks, float scale, attn_dtype dtype, void* stream);
 
 /* Static string naming a status code. */
 const char* attn_status_string(attn_status s);

@@ -41,6 +41,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+                            "attn_kv_append", "attn_paged_prefill",
                             "attn_status_string", "attn_last_error", "attn_abi_version"])
 
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -116,6 +117,57 @@ def test_workspace_size(lib):
     assert lib.attn_paged_decode_workspace_size(0, 1, 64, 1, 16) == 0
 
 
+def app(lib, kn=A, vn=A + 16 * MB, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB,
+        ctx=A + 200 * MB, starts=A + 201 * MB, bs=16, S=4, T=40, max_new=10, Hkv=2, d=128,
+        max_blocks=8, num_blocks=32, dtype=BF16):
+    return lib.attn_kv_append(kn, vn, kc, vc, table, ctx, starts, bs, S, T, max_new, Hkv, d,
+                              max_blocks, num_blocks, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=0), INVALID), (dict(vc=0), INVALID), (dict(starts=0), INVALID), (dict(S=0), INVALID),
+    (dict(Hkv=0), INVALID), (dict(num_blocks=0), INVALID), (dict(T=-1), INVALID),
+    (dict(max_new=-1), INVALID), (dict(dtype=5), UNSUPPORTED), (dict(d=4), UNSUPPORTED),
+    (dict(d=4096), UNSUPPORTED), (dict(bs=0), UNSUPPORTED), (dict(bs=2048), UNSUPPORTED),
+    (dict(S=70000), UNSUPPORTED), (dict(kn=A + 8), INVALID), (dict(kc=A + 64 * MB + 4), INVALID),
+    (dict(ctx=A + 200 * MB + 2), INVALID), (dict(vc=A + 64 * MB + 1024), INVALID),
+    (dict(kc=A), INVALID), (dict(vc=A + 200 * MB - 4096), INVALID),
+])
+def test_append_rejects_before_any_launch(lib, kw, status):
+    assert app(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_append_with_nothing_to_write_launches_nothing(lib):
+    # valid arguments with T = 0 or max_new = 0 return OK without any HIP call
+    assert app(lib, T=0) == OK and app(lib, max_new=0) == OK
+    assert app(lib, dtype=F32, d=64, T=0) == OK
+
+
+def ppf(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A + 200 * MB,
+        starts=A + 201 * MB, bs=16, o=A + 208 * MB, lse=A + 216 * MB, S=4, T=40, max_new=10, Hq=12,
+        Hkv=2, d=128, max_blocks=8, num_blocks=32, scale=0.088, dtype=BF16):
+    return lib.attn_paged_prefill(q, kc, vc, table, ctx, starts, bs, o, lse, S, T, max_new, Hq,
+                                  Hkv, d, max_blocks, num_blocks, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(starts=0), INVALID), (dict(o=0), INVALID), (dict(S=0), INVALID),
+    (dict(Hq=12, Hkv=5), INVALID), (dict(T=-3), INVALID), (dict(max_new=-1), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(dtype=F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED), (dict(max_new=1 << 20, Hq=64), UNSUPPORTED),
+    (dict(q=A + 4), INVALID), (dict(starts=A + 201 * MB + 1), INVALID), (dict(lse=A + 216 * MB + 2), INVALID),
+    (dict(o=A + 64 * MB), INVALID), (dict(lse=A + 200 * MB), INVALID), (dict(lse=A + 208 * MB), INVALID),
+])
+def test_paged_prefill_rejects_before_any_launch(lib, kw, status):
+    assert ppf(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_paged_prefill_with_no_rows_launches_nothing(lib):
+    assert ppf(lib, T=0) == OK and ppf(lib, max_new=0) == OK
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd") or torch.cuda.is_available()
 
@@ -124,6 +176,8 @@ def _gpu_present():
 def test_no_device_status(lib):
     assert fwd(lib) == NO_DEVICE
     assert dec(lib) == NO_DEVICE
+    assert app(lib) == NO_DEVICE
+    assert ppf(lib) == NO_DEVICE
 
 
 def test_binding_rejects_host_tensors():
