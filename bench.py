@@ -12,7 +12,11 @@ inputs:
 `value` is the prefill's attention-forward throughput in TFLOP/s
 (algorithmic flops 4*d*Hq*T(T+1)/2 over the average kernel time measured
 with HIP events on the launch stream); the decode's GB/s (algorithmic bytes
-over its average time) is reported beside it.  Prints ONE JSON line.
+over its average time) is reported beside it.  The steps either side of
+decode are timed after the main loop, on the same 64-sequence cache: the
+chunked prefill of 256 new rows per sequence (attn_paged_prefill) and the
+append of those rows' keys and values (attn_kv_append).  Prints ONE JSON
+line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -59,6 +63,36 @@ def decode_bytes(p, cfg) -> float:
 
 def decode_flops(p, cfg) -> float:
     return 4.0 * cfg.Hq * cfg.d * float(p["ctx_lens"].numpy().astype(np.int64).sum())
+
+
+def chunked_flops(p, cfg) -> float:
+    """Row t of a sequence with n new rows and length L attends L - n + t + 1 keys."""
+    ctx = p["ctx_lens"].numpy().astype(np.int64)
+    n = p["new_lens"].numpy().astype(np.int64)
+    pairs = float((n * (ctx - n) + n * (n + 1) // 2).sum())
+    return 4.0 * cfg.Hq * cfg.d * pairs
+
+
+def chunked_bytes(p, cfg) -> float:
+    """K and V of every cached position once per kv head, the new rows' q,
+    o and lse, the used table entries, the lengths and the row offsets."""
+    ctx = p["ctx_lens"].numpy().astype(np.int64)
+    T = int(p["starts"][-1])
+    kv = int(ctx.sum()) * cfg.Hkv * cfg.d * 2 * 2
+    table = int(((ctx + cfg.block_size - 1) // cfg.block_size).sum()) * 4
+    return kv + 2 * T * cfg.Hq * cfg.d * 2 + T * cfg.Hq * 4 + table + cfg.S * 4 + (cfg.S + 1) * 4
+
+
+def append_bytes(p, cfg) -> float:
+    """The new rows' K and V read once and written once, plus the lengths,
+    row offsets and the table entries they land in."""
+    T = int(p["starts"][-1])
+    rows = 2 * T * cfg.Hkv * cfg.d * 2
+    ctx = p["ctx_lens"].numpy().astype(np.int64)
+    n = p["new_lens"].numpy().astype(np.int64)
+    blocks = int(((ctx + cfg.block_size - 1) // cfg.block_size
+                  - (ctx - n) // cfg.block_size).sum())
+    return 2 * rows + cfg.S * 4 + (cfg.S + 1) * 4 + blocks * 4
 
 
 def profiled_traffic(profile: str, sources) -> float | None:
@@ -137,8 +171,10 @@ def main(argv=None):
 
     import torch
     from exact_tiled_self_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
+    from exact_tiled_self_amd import attn_kv_append, attn_paged_prefill
     from exact_tiled_self_amd import _lib
-    from exact_tiled_self_amd.inputs import DENSE_CONFIGS, PAGED_CONFIG, dense_inputs, paged_inputs
+    from exact_tiled_self_amd.inputs import (CHUNK_NEW, DENSE_CONFIGS, PAGED_CONFIG, chunked_inputs,
+                                             dense_inputs)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -148,7 +184,7 @@ def main(argv=None):
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
     lse = torch.empty(pcfg.B, pcfg.Hq, pcfg.N, dtype=torch.float32, device=dev)
-    p = paged_inputs(dcfg)
+    p = chunked_inputs(dcfg, new_lens=CHUNK_NEW)       # the decode cache plus a chunk per sequence
     pd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in p.items()}
     od = torch.empty_like(pd["q"])
     lsed = torch.empty(dcfg.S, dcfg.Hq, dtype=torch.float32, device=dev)
@@ -223,6 +259,37 @@ def main(argv=None):
         g_ms.append(e0.elapsed_time(e1) / 8)
     del dg
 
+    # the steps either side of decode, on the same cache: chunked prefill of
+    # CHUNK_NEW rows per sequence, and the append of those rows' K/V into a
+    # copy of the cache (the append rewrites the slots it targets)
+    oc = torch.empty_like(pd["q_new"])
+    lsec = torch.empty(pd["q_new"].shape[:2], dtype=torch.float32, device=dev)
+    kc2, vc2 = pd["k_cache"].clone(), pd["v_cache"].clone()
+
+    def chunked():
+        attn_paged_prefill(pd["q_new"], pd["k_cache"], pd["v_cache"], pd["block_table"], pd["ctx_lens"],
+                           pd["starts"], 16, dcfg.scale, max_new=p["max_new"], o=oc, lse=lsec,
+                           stream=stream)
+
+    def append():
+        attn_kv_append(pd["k_new"], pd["v_new"], kc2, vc2, pd["block_table"], pd["ctx_lens"],
+                       pd["starts"], 16, max_new=p["max_new"], stream=stream)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        e[0].record(stream)
+        for i in range(reps):
+            fn()
+            e[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [e[i].elapsed_time(e[i + 1]) for i in range(reps)]
+
+    ch_ms = timed(chunked, K)
+    ap_ms = timed(append, K)
+    del kc2, vc2
+
     # parity spot check on the benchmarked buffers (sampled rows / sequences)
     from oracle import exact as OA
     rows = np.array([0, 1, 4095, 8190, 8191])
@@ -236,6 +303,12 @@ def main(argv=None):
                              p["v_cache"].float().numpy(), p["block_table"].numpy()[sub],
                              p["ctx_lens"].numpy()[sub], 16, dcfg.scale)
     derr = float(np.abs(od[torch.as_tensor(sub)].double().cpu().numpy() - ro).max())
+    st = p["starts"].numpy().astype(np.int64)
+    cs = int(p["ctx_lens"].numpy().argmax())
+    ro, rl = OA.paged_prefill(p["q_new"][st[cs]:st[cs + 1]].double().numpy(), p["k_cache"].float().numpy(),
+                              p["v_cache"].float().numpy(), p["block_table"].numpy()[cs:cs + 1],
+                              p["ctx_lens"].numpy()[cs:cs + 1], [0, st[cs + 1] - st[cs]], 16, dcfg.scale)
+    cerr = float(np.abs(oc[st[cs]:st[cs + 1]].double().cpu().numpy() - ro).max())
 
     clocks = read_clocks()
 
@@ -246,6 +319,9 @@ def main(argv=None):
     dec_avg = float(np.mean(dec_ms))
     gbps = db / (dec_avg * 1e-3) / 1e9
     fl_avg = float(np.mean(fl_ms))
+    cf, cb = chunked_flops(p, dcfg), chunked_bytes(p, dcfg)
+    ch_avg, ap_avg = float(np.mean(ch_ms)), float(np.mean(ap_ms))
+    ab = append_bytes(p, dcfg)
 
     out = {
         "metric": METRIC,
@@ -271,7 +347,8 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("prefill_bf16_d128_causal_gqa_t8192",
-                                                 ["prefill_bf16.hip", "common.h", "internal.h"]),
+                                                 ["prefill_bf16.hip", "prefill_tile.h", "common.h",
+                                                  "internal.h"]),
                      "algorithmic_bytes": prefill_bytes(pcfg),
                      "kernel": "prefill_bf16_kernel<128, causal>",
                      "per_launch": {"flops": pf, "avg_us": round(pre_avg * 1e3, 2),
@@ -288,8 +365,25 @@ def main(argv=None):
                    "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
                    "traffic": profiled_traffic("paged_decode_bf16_d128_s64",
                                                ["decode_paged.hip", "common.h", "internal.h"])},
+        "chunked_prefill": {
+            "workload": f"paged_decode_s64 cache, {CHUNK_NEW} new rows per sequence (T={int(st[-1])})",
+            "value": round(cf / (ch_avg * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "frac_mfma": round(cf / (ch_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_us": round(ch_avg * 1e3, 2), "median_us": round(float(np.median(ch_ms)) * 1e3, 2),
+            "min_us": round(min(ch_ms) * 1e3, 2), "flops": cf, "algorithmic_bytes": cb,
+            "kernel": "prefill_paged_kernel<128>",
+            "traffic": profiled_traffic("chunked_prefill_bf16_d128_s64_c256",
+                                        ["prefill_paged.hip", "prefill_tile.h", "common.h", "internal.h"])},
+        "kv_append": {
+            "workload": f"{CHUNK_NEW} new rows per sequence into the paged_decode_s64 cache",
+            "value": round(ab / (ap_avg * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac_hbm": round(ab / (ap_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "avg_us": round(ap_avg * 1e3, 2), "median_us": round(float(np.median(ap_ms)) * 1e3, 2),
+            "min_us": round(min(ap_ms) * 1e3, 2), "bytes": ab, "kernel": "kv_append_kernel",
+            "traffic": profiled_traffic("kv_append_bf16_d128_s64_c256",
+                                        ["kv_append.hip", "common.h", "internal.h"])},
         "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,
-                   "tolerance": 2e-2},
+                   "chunked_prefill_sampled_max_abs": cerr, "tolerance": 2e-2},
         "wall_s_timed": round(wall, 3),
         "clocks_after_timing": clocks,
         "library": _lib.library_path(),

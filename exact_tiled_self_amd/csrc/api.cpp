@@ -260,7 +260,7 @@ attn_status attn_paged_prefill(const void* q, const void* k_cache, const void* v
     if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
     if ((long long)max_new * Hq * d * 2 >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "max_new * Hq * d * 2 must be below 2^31");
-    if ((long long)((max_new + 127) / 128) * S * Hq >= (1LL << 31))
+    if ((long long)((max_new + 127) / 128) * S * Hq + 8LL * Hq >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
     if ((long long)num_blocks * Hkv * block_size * d >= (1LL << 40))
         return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");

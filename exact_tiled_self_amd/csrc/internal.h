@@ -9,6 +9,10 @@
 
 namespace attn {
 
+// XCDs of an MI355X: workgroup b of a launch is dispatched to XCD b % kXcds,
+// and each XCD has its own L2.
+constexpr int kXcds = 8;
+
 struct PrefillArgs {
     const void* q;
     const void* k;

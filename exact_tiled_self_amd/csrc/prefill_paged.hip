@@ -18,9 +18,13 @@
 // 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in
 // LDS, K loaded straight into LDS, V stored transposed, MFMA 32x32x16 bf16
 // on S^T = K Q^T and O^T += V^T P^T, lazy rescale of the running maximum.
-// The work units are (query tile, sequence, query head), later query tiles
-// first (they see the most keys), heads fastest so the heads that share a
-// kv head run side by side and share its tiles in L2.
+// The work units are (query tile, sequence, query head), heads fastest.
+// Sequence lengths vary widely, so the (query tile, sequence) pairs run
+// longest first: every workgroup ranks the pairs by the number of keys their
+// last row sees, read from the device-resident lengths (up to 512 pairs;
+// beyond that, later query tiles first).  The block -> unit map sends the
+// heads that share a kv head to one XCD, side by side, so they share its
+// tiles in that XCD's L2.
 //
 // Device-resident values are checked before they form an address: a
 // sequence with malformed row offsets (or more than max_new rows) is left
@@ -34,6 +38,9 @@
 namespace attn {
 namespace {
 
+// Up to this many (q tile, sequence) pairs, every workgroup ranks them by
+// cost to run the longest first (P^2 / 256 comparisons per thread).
+constexpr int kRankPairs = 512;
 constexpr uint32_t kNaNBf16x2 = 0x7FC07FC0u;   // two quiet bf16 NaNs
 constexpr uint32_t kNaN32 = 0x7FC00000u;       // quiet fp32 NaN
 
@@ -50,19 +57,55 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     static_assert(PF_BN == PF_WAVES * BS, "one cache block per wave per key tile");
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
     __shared__ int bad_s[PF_WAVES];
+    __shared__ int rank_cost[kRankPairs];
+    __shared__ int rank_pick;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
 
-    // Work unit: (q tile, sequence, head), latest q tiles first.
+    // Work unit: (q tile, sequence, head), latest q tiles first, heads
+    // fastest.  Workgroup b runs on XCD b % 8; the j-th workgroup of XCD x
+    // takes unit (j / G) * 8G + x * G + j % G, so the G heads that share a kv
+    // head (one aligned run of G units) run on one XCD and share its L2.
+    const int G = Hq / Hkv;
+    const int xcd = blockIdx.x & (kXcds - 1), jx = blockIdx.x / kXcds;
+    const int wg = (jx / G) * (kXcds * G) + xcd * G + jx % G;
     const int SH = S * Hq;
-    const int wg = blockIdx.x;
-    const int qt = n_qtiles - 1 - wg / SH;
-    const int sh = wg - (wg / SH) * SH;
-    const int s = sh / Hq, h = sh - s * Hq;
-    const int g = h / (Hq / Hkv);
+    if (wg >= n_qtiles * SH) return;
+    const int h = wg % Hq, g = h / G;
+    int qt, s;
+    const int P = n_qtiles * S;                               // (q tile, sequence) pairs
+    if (P <= kRankPairs) {
+        // Longest first: the pair of rank wg / Hq in decreasing order of the
+        // keys its last row sees (ties by pair index), from the lengths.
+        for (int i = tid; i < P; i += PF_THREADS) {
+            const int qi = i / S, si = i - qi * S;
+            const int ai = starts[si], bi = starts[si + 1], ci = ctx_lens[si];
+            const int ni = bi - ai;
+            const bool runs = !(ai < 0 || bi > T || ni < 0 || ni > max_new) && qi * PF_BM < ni;
+            const bool sane = ci >= ni && ci <= max_blocks * kDecodeBlock;
+            rank_cost[i] = !runs ? -1 : (sane ? ci - ni + min(qi * PF_BM + PF_BM, ni) : 0);
+        }
+        __syncthreads();
+        const int want = wg / Hq;
+        for (int i = tid; i < P; i += PF_THREADS) {
+            const int ci = rank_cost[i];
+            int r = 0;
+            for (int j = 0; j < P; ++j) {
+                const int cj = rank_cost[j];
+                r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
+            }
+            if (r == want) rank_pick = i;
+        }
+        __syncthreads();
+        qt = rank_pick / S;
+        s = rank_pick - qt * S;
+    } else {
+        qt = n_qtiles - 1 - wg / SH;                          // later q tiles first
+        s = (wg - (wg / SH) * SH) / Hq;
+    }
 
     const int a = starts[s], b = starts[s + 1], ctx = ctx_lens[s];
     const int n = b - a;
@@ -216,7 +259,9 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 template <int D>
 hipError_t launch_paged_prefill_t(const PagedPrefillArgs& a, hipStream_t stream) {
     const int n_qt = (a.max_new + PF_BM - 1) / PF_BM;
-    const dim3 grid((unsigned)(n_qt * a.S * a.Hq)), block(PF_THREADS);
+    const long long units = (long long)n_qt * a.S * a.Hq;
+    const long long per_round = (long long)kXcds * (a.Hq / a.Hkv);      // whole runs on every XCD
+    const dim3 grid((unsigned)((units + per_round - 1) / per_round * per_round)), block(PF_THREADS);
     hipLaunchKernelGGL((prefill_paged_kernel<D>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, a.starts,
