@@ -159,6 +159,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the rocm-smi clock readout (a child process; under a counter "
+                         "profiler every process initialises the GPU)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -310,7 +313,7 @@ def main(argv=None):
                               p["ctx_lens"].numpy()[cs:cs + 1], [0, st[cs + 1] - st[cs]], 16, dcfg.scale)
     cerr = float(np.abs(oc[st[cs]:st[cs + 1]].double().cpu().numpy() - ro).max())
 
-    clocks = read_clocks()
+    clocks = None if args.no_clocks else read_clocks()
 
     pf = prefill_flops(pcfg)
     pre_avg = float(np.mean(pre_ms))
