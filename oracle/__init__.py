@@ -16,11 +16,14 @@ recurrence  a scalar model of the block-by-block online-softmax recurrence
             warn against
 kvcache     appending new tokens' keys and values to a paged KV cache,
             one token at a time through the block table
+backward    the gradients dq, dk, dv of the exact attention (chain rule
+            through o = P V and the softmax, weights recomputed from q, k)
 
 Sources (web pages; cited by title and section):
   [AT]  "Autoatención, kernels CUDA y FlashAttention", section 1 (how
         self-attention works in a vision transformer) and section 3
-        (FlashAttention: tiling, online softmax, saved statistics)
+        (FlashAttention: tiling, online softmax, saved statistics,
+        recomputation in the backward pass)
   [FA]  "FlashAttention" (notes page), sections "Mecanismo y detalles" and
         "No basta con promediar los resultados de los bloques"
   [KR]  "Kernels de atención rápida y fusión de operadores" (the-ai.news),
@@ -40,3 +43,4 @@ from .recurrence import (  # noqa: F401
     naive_block_average,
 )
 from .kvcache import append_paged  # noqa: F401
+from .backward import attention_bwd  # noqa: F401
