@@ -7,7 +7,8 @@ library; the first call does, and raises if it is missing.
 """
 
 __all__ = ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-           "attn_kv_append", "attn_paged_prefill", "AttnError", "library_path", "abi_version"]
+           "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size",
+           "AttnError", "library_path", "abi_version"]
 
 
 def __getattr__(name):

@@ -19,7 +19,7 @@ import torch
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-           "attn_kv_append", "attn_paged_prefill", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
+           "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_BF16"]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_NO_DEVICE, ATTN_ERR_LAUNCH = range(5)
@@ -67,6 +67,11 @@ def raw_library():
         lib.attn_paged_prefill.restype = ci
         lib.attn_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci,
                                            ci, ci, ci, cf, ci, vp]
+        lib.attn_bwd_workspace_size.restype = sz
+        lib.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci]
+        lib.attn_bwd.restype = ci
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp,
+                                 sz, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ci]
         lib.attn_last_error.restype = ctypes.c_char_p
@@ -229,3 +234,37 @@ def attn_paged_prefill(q, k_cache, v_cache, block_table, ctx_lens, starts, block
         _DTYPE[q.dtype], _stream_ptr(q.device, stream))
     _check(st)
     return o, lse
+
+
+def attn_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
+    return int(raw_library().attn_bwd_workspace_size(B, Hq, Hkv, N, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, *, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd, recomputing the weights from q, k
+    and the forward's lse.  q, o, dout: [B, Hq, N, d] bf16; k, v: [B, Hkv, N, d]
+    bf16; lse: [B, Hq, N] float32 (as attn_fwd returned it)."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v, o and dout must share dtype")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
+        raise ValueError("inconsistent shapes, or lse not float32 [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_bwd_workspace_size(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = raw_library().attn_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(lse, "lse"), _dev(dout, "dout"),
+        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, Hq, Hkv, N, d, float(scale),
+        int(bool(causal)), _DTYPE[q.dtype], _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q.device, stream))
+    _check(st)
+    return dq, dk, dv

@@ -23,7 +23,7 @@ LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "prefill_paged.hip",
-           "kv_append.hip"]
+           "kv_append.hip", "backward_bf16.hip"]
 
 # Device-code flags: gfx950 only; packed fp32 instructions disabled.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -36,6 +36,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 EXTRA_FLAGS = {
     "prefill_bf16.hip": ["-fno-honor-nans"],
     "prefill_paged.hip": ["-fno-honor-nans"],
+    "backward_bf16.hip": ["-fno-honor-nans"],
     # matrix-core accumulators in ordinary VGPRs: the decode loop rescales
     # them every block, which in AGPRs costs a read and a write per element
     "decode_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -291,4 +291,61 @@ attn_status attn_paged_prefill(const void* q, const void* k_cache, const void* v
     return launch_status(attn::launch_paged_prefill_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0) return 0;
+    return attn::bwd_workspace_bytes(B, Hq, Hkv, N, d);
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                     float scale, int causal, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    g_err[0] = '\0';
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-null");
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "B, Hq, Hkv and N must be >= 1 (got %d, %d, %d, %d)", B, Hq, Hkv, N);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
+    if ((long long)N * d > (1LL << 31) - (1LL << 16))
+        return fail(ATTN_ERR_UNSUPPORTED, "N * d must be at most 2^31 - 2^16");
+    const long long grid = (long long)B * Hq * ((N + 127) / 128);
+    if (grid >= (1LL << 31) || (long long)B * Hq * N * (d / 8) >= (1LL << 38))
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, dout, dq, dk, dv and workspace must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const size_t qb = (size_t)B * Hq * N * d * 2, kb = (size_t)B * Hkv * N * d * 2, lb = (size_t)B * Hq * N * 4;
+    const void* ins[6] = {q, k, v, o, lse, dout};
+    const size_t insz[6] = {qb, kb, kb, qb, lb, qb};
+    const void* outs[4] = {dq, dk, dv, workspace};
+    const size_t outsz[4] = {qb, kb, kb, need};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], outsz[i], ins[j], insz[j]))
+                return fail(ATTN_ERR_INVALID_ARG, "outputs and workspace must not overlap the inputs");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outsz[i], outs[j], outsz[j]))
+                return fail(ATTN_ERR_INVALID_ARG, "dq, dk, dv and workspace must not overlap");
+    }
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+
+    attn::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d;
+    a.scale = scale; a.causal = causal;
+    a.workspace = static_cast<float*>(workspace);
+    return launch_status(attn::launch_backward_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

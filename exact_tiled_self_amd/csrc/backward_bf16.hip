@@ -1,0 +1,540 @@
+// Attention backward pass with recomputation, bf16 in / bf16 out, fp32
+// accumulation, for gfx950.
+//
+// The forward keeps only o and lse = m + ln l per row; the backward
+// recomputes the weights p_ij = e^(scale*<q_i,k_j> - lse_i) tile by tile from
+// q, k and lse instead of reading a stored N x N matrix
+// ("Autoatención, kernels CUDA y FlashAttention", section 3, recomputation
+// in the backward pass).  With D_i = <do_i, o_i>:
+//
+//   dv_j = sum_i p_ij do_i,   dp_ij = <do_i, v_j>,   ds_ij = p_ij (dp_ij - D_i)
+//   dq_i = scale * sum_j ds_ij k_j,   dk_j = scale * sum_i ds_ij q_i
+//
+// Four kernels, none with atomics (results are deterministic):
+//   * bwd_prep: D_i from o and do (fp32), into the workspace.
+//   * bwd_dq: 4 waves x 32 query rows, key tiles of 32; per tile S^T = K Q^T
+//     and dP^T = V dO^T on MFMA (a lane owns one query row, so lse_i and D_i
+//     are per-lane scalars), dS^T in registers, then dQ^T += K^T dS^T with
+//     dS^T taken straight from the accumulators as the B operand.  K and V
+//     are staged row-major (XOR-swizzled 16-byte chunks) and K^T transposed
+//     with the accumulator key order (bits 2 and 3 of the key swapped).
+//   * bwd_dkdv: 4 waves x 32 keys, query chunks of 32; per chunk S = Q K^T
+//     and dP = dO V^T (a lane owns one key; its K and V rows stay in
+//     registers), P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS.
+//     Q and dO are staged row-major and transposed; lse and D per query go
+//     through LDS.
+//   * bwd_reduce: with grouped K/V heads the dkdv kernel writes one fp32
+//     dk, dv per query head into the workspace and this kernel sums each
+//     group in head order into the bf16 outputs.
+// Causal tiles entirely outside the triangle are never visited; the heaviest
+// tiles are dispatched first.
+
+#include "internal.h"
+#include "prefill_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr int BW_THREADS = 256;
+constexpr int BW_T = 32;                  // keys per dq tile / queries per dkdv chunk
+constexpr float kInf = __builtin_inff();
+
+// One staged 32 x D tile: row-major with XOR-swizzled 16-byte chunks, and
+// transposed ([D][32 + 8]) with the accumulator order of the 32 rows.
+template <int D>
+struct BwTile {
+    static constexpr int CPR = D / 8;
+    static constexpr int TSTR = BW_T + 8;            // bf16 per transposed row (16-B pad)
+    static constexpr int ROW = BW_T * D;             // row-major elements
+    static constexpr int TRN = D * TSTR;             // transposed elements
+    static constexpr int NST = BW_T * D / 16;        // threads staging it (2 rows x 8 dims each)
+};
+
+// Row-major 16-byte chunk (row r, logical chunk cc) position in elements.
+template <int D>
+__device__ __forceinline__ int bw_rm(int r, int cc) {
+    return r * D + ((cc ^ kswz<D / 8>(r)) * 8);
+}
+
+// Thread t < NST holds rows 2*(t % 16) + {0, 1}, dims 8*(t / 16) .. +7 of a
+// tile: write them row-major and transposed.
+template <int D>
+__device__ __forceinline__ void bw_store_both(uint16_t* rm, uint16_t* tr, const u32x4* x, int t) {
+    using L = BwTile<D>;
+    const int kq = t % 16, vdc = t / 16;
+    const int r0 = 2 * kq;
+    *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0, vdc)) = x[0];
+    *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0 + 1, vdc)) = x[1];
+    const int pos = swap23(r0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        *reinterpret_cast<uint32_t*>(tr + (vdc * 8 + j) * L::TSTR + pos) =
+            __builtin_amdgcn_perm(x[1][w], x[0][w], sel);
+    }
+}
+
+// ------------------------------------------------------------------ prep --
+
+template <int D>
+__global__ void __launch_bounds__(BW_THREADS)
+bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                float* __restrict__ delta, long long rows) {
+    constexpr int LPR = D / 8;                       // lanes per row
+    const long long row = ((long long)blockIdx.x * BW_THREADS + threadIdx.x) / LPR;
+    const int c = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = ld16(o + row * D + c * 8);
+        const u32x4 b = ld16(dout + row * D + c * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = fmaf(bf16_to_f32((uint16_t)(a[w] & 0xffff)), bf16_to_f32((uint16_t)(b[w] & 0xffff)), acc);
+            acc = fmaf(bf16_to_f32((uint16_t)(a[w] >> 16)), bf16_to_f32((uint16_t)(b[w] >> 16)), acc);
+        }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && c == 0) delta[row] = acc;
+}
+
+// -------------------------------------------------------------------- dq --
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+              const float* __restrict__ lse, const float* __restrict__ delta,
+              uint16_t* __restrict__ dq, int Hq, int Hkv, int N, int BH, int n_qtiles, float c,
+              float scale) {
+    using L = BwTile<D>;
+    constexpr int STAGE = 2 * L::ROW + L::TRN;       // K, V row-major + K^T
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, l32 = lane & 31;
+
+    const int wg = blockIdx.x;
+    const int qt = CAUSAL ? (n_qtiles - 1 - wg / BH) : (wg / BH);
+    const int bh = wg % BH;
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dout + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+
+    const int q0 = qt * PF_BM;
+    const int wrow0 = q0 + wave * 32;
+    const int myrow = wrow0 + l32;
+    const bool wave_active = wrow0 < N;
+    const bool row_ok = myrow < N;
+
+    // q and do rows as B operands (dims 16*ks + 8*hi .. +7), lse in base 2, D.
+    bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t off = (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2;
+        qf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(qrs, off));
+        gf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(ors, off));
+    }
+    const float lse2 = row_ok ? lse[(size_t)bh * N + myrow] * kLog2e : kInf;
+    const float drow = row_ok ? delta[(size_t)bh * N + myrow] : 0.f;
+
+    const int row_end = min(q0 + PF_BM, N);
+    const int n_kt = CAUSAL ? (row_end + BW_T - 1) / BW_T : (N + BW_T - 1) / BW_T;
+
+    // Staging: thread t < NST loads K rows 2*(t%16) + {0,1}, dims 8*(t/16)..+7
+    // into registers (written row-major and transposed); V goes straight to
+    // LDS, chunk p = i * 256 + tid of the tile.
+    constexpr int VINST = L::ROW / 8 / BW_THREADS;   // 2 (D = 128) or 1 (D = 64)
+    const bool kst = tid < L::NST;
+    const uint32_t koff = (uint32_t)((2 * (tid % 16)) * D + (tid / 16) * 8) * 2;
+    uint32_t voff[VINST];
+#pragma unroll
+    for (int i = 0; i < VINST; ++i) {
+        const int p = (i * PF_WAVES + wave) * 64 + lane;
+        const int r = p / L::CPR;
+        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
+        voff[i] = (uint32_t)(r * D + cc * 8) * 2;
+    }
+    u32x4 kreg[2];
+
+    auto issue_loads = [&](int kt, int buf) {
+        const uint32_t t0 = (uint32_t)kt * BW_T * D * 2;
+        uint16_t* Vs = smem + buf * STAGE + L::ROW;
+#pragma unroll
+        for (int i = 0; i < VINST; ++i)
+            buf_ld16_lds(vrs, Vs + (i * PF_WAVES + wave) * 64 * 8, t0 + voff[i]);
+        if (kst) {
+            kreg[0] = buf_ld16(krs, t0 + koff);
+            kreg[1] = buf_ld16(krs, t0 + koff + D * 2);
+        }
+    };
+    auto store_k = [&](int buf) {
+        if (kst) bw_store_both<D>(smem + buf * STAGE, smem + buf * STAGE + 2 * L::ROW, kreg, tid);
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    store_k(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < n_kt;
+        if (more) issue_loads(kt + 1, buf ^ 1);
+        const int k0 = kt * BW_T;
+        if (wave_active && (!CAUSAL || k0 <= wrow0 + 31)) {
+            const uint16_t* Ks = smem + buf * STAGE;
+            const uint16_t* Vs = Ks + L::ROW;
+            const uint16_t* Kt = Ks + 2 * L::ROW;
+            // S^T = K Q^T and dP^T = V dO^T for the tile's 32 keys.
+            f32x16 sacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int e = bw_rm<D>(l32, ks * 2 + hi);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + e);
+                const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + e);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], pacc, 0, 0, 0);
+            }
+            // dS^T = P^T (dP^T - D), P^T = 2^(c s - lse2); key of entry r:
+            // k0 + 8(r/4) + 4hi + r%4.
+            const bool need_mask = (k0 + BW_T > N) || (CAUSAL && k0 + BW_T - 1 > wrow0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(sacc[r], c, -lse2));
+                if (need_mask) {
+                    const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= myrow);
+                    p = ok ? p : 0.f;
+                }
+                sacc[r] = p * (pacc[r] - drow);
+            }
+            // dQ^T += K^T dS^T, 16 keys per MFMA.
+#pragma unroll
+            for (int c16 = 0; c16 < BW_T / 16; ++c16) {
+                bf16x8 sb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sb[i] = (__bf16)sacc[c16 * 8 + i];
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        Kt + (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[db], 0, 0, 0);
+                }
+            }
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);
+            store_k(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    if (row_ok) {
+        uint16_t* orow = dq + ((size_t)bh * N + myrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int dim0 = db * 32 + rg * 8 + hi * 4;
+                const u32x2 w = {pack_bf16x2(acc[db][rg * 4 + 0] * scale, acc[db][rg * 4 + 1] * scale),
+                                 pack_bf16x2(acc[db][rg * 4 + 2] * scale, acc[db][rg * 4 + 3] * scale)};
+                *reinterpret_cast<u32x2*>(orow + dim0) = w;
+            }
+    }
+}
+
+// ------------------------------------------------------------------ dkdv --
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                const float* __restrict__ lse, const float* __restrict__ delta,
+                uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dk32,
+                float* __restrict__ dv32, int Hq, int Hkv, int N, int BH, int n_ktiles, float c,
+                float scale) {
+    using L = BwTile<D>;
+    constexpr int STAGE = 2 * (L::ROW + L::TRN) + 2 * BW_T * 2;   // Q, dO both ways + lse2, D
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, l32 = lane & 31;
+
+    // Work unit (b, h, 128-key tile); with a causal mask the first key tiles
+    // see the most queries and go first.
+    const int wg = blockIdx.x;
+    const int kt = wg / BH;
+    const int bh = wg % BH;
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dout + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    (void)n_ktiles;
+
+    const int key0 = kt * PF_BM;
+    const int wkey0 = key0 + wave * 32;
+    const int mykey = wkey0 + l32;
+    const bool wave_active = wkey0 < N;
+
+    // This lane's key row of K and V as B operands (dims 16*ks + 8*hi .. +7).
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t off = (uint32_t)(mykey * D + ks * 16 + hi * 8) * 2;
+        kf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(krs, off));
+        vf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(vrs, off));
+    }
+
+    // Query chunks: all of them, or (causal) those with a query >= key0.
+    const int c_first = CAUSAL ? key0 / BW_T : 0;
+    const int n_c = (N + BW_T - 1) / BW_T;
+
+    const bool st = tid < L::NST;
+    const uint32_t soff = (uint32_t)((2 * (tid % 16)) * D + (tid / 16) * 8) * 2;
+    u32x4 qreg[2], greg[2];
+    float lreg = 0.f, dreg = 0.f;
+    const float* lse_h = lse + (size_t)bh * N;
+    const float* del_h = delta + (size_t)bh * N;
+
+    auto issue_loads = [&](int cj) {
+        const uint32_t t0 = (uint32_t)cj * BW_T * D * 2;
+        if (st) {
+            qreg[0] = buf_ld16(qrs, t0 + soff);
+            qreg[1] = buf_ld16(qrs, t0 + soff + D * 2);
+            greg[0] = buf_ld16(ors, t0 + soff);
+            greg[1] = buf_ld16(ors, t0 + soff + D * 2);
+        }
+        if (tid < BW_T) {
+            const int qi = cj * BW_T + tid;
+            lreg = qi < N ? lse_h[qi] * kLog2e : kInf;
+            dreg = qi < N ? del_h[qi] : 0.f;
+        }
+    };
+    auto store = [&](int buf) {
+        uint16_t* base = smem + buf * STAGE;
+        if (st) {
+            bw_store_both<D>(base, base + 2 * L::ROW, qreg, tid);
+            bw_store_both<D>(base + L::ROW, base + 2 * L::ROW + L::TRN, greg, tid);
+        }
+        if (tid < BW_T) {
+            float* stats = reinterpret_cast<float*>(base + 2 * (L::ROW + L::TRN));
+            stats[tid] = lreg;
+            stats[BW_T + tid] = dreg;
+        }
+    };
+
+    f32x16 kacc[D / 32], vacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { kacc[db][r] = 0.f; vacc[db][r] = 0.f; }
+
+    if (c_first < n_c) {
+        issue_loads(c_first);
+        __builtin_amdgcn_s_waitcnt(0);
+        store(0);
+    }
+    __syncthreads();
+
+    for (int cj = c_first; cj < n_c; ++cj) {
+        const int buf = (cj - c_first) & 1;
+        const bool more = cj + 1 < n_c;
+        if (more) issue_loads(cj + 1);
+        const int qc = cj * BW_T;
+        // skip a chunk whose queries all precede this wave's keys
+        if (wave_active && (!CAUSAL || qc + BW_T - 1 >= wkey0)) {
+            const uint16_t* Qs = smem + buf * STAGE;
+            const uint16_t* Gs = Qs + L::ROW;
+            const uint16_t* Qt = Qs + 2 * L::ROW;
+            const uint16_t* Gt = Qt + L::TRN;
+            const float* stats = reinterpret_cast<const float*>(Qs + 2 * (L::ROW + L::TRN));
+            // S = Q K^T and dP = dO V^T: lane = key, entry r = query
+            // qc + 8(r/4) + 4hi + r%4.
+            f32x16 sacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int e = bw_rm<D>(l32, ks * 2 + hi);
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + e);
+                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + e);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
+            }
+            const bool need_mask = (qc + BW_T > N) || (mykey >= N) ||
+                                   (CAUSAL && qc < wkey0 + 31);
+            f32x16 pv;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + BW_T + 8 * rg + 4 * hi);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rg * 4 + i;
+                    float p = fast_exp2(fmaf(sacc[r], c, -l4[i]));
+                    if (need_mask) {
+                        const int qi = qc + 8 * rg + 4 * hi + i;
+                        const bool ok = qi < N && mykey < N && (!CAUSAL || mykey <= qi);
+                        p = ok ? p : 0.f;
+                    }
+                    pv[r] = p;
+                    sacc[r] = p * (pacc[r] - d4[i]);
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
+#pragma unroll
+            for (int c16 = 0; c16 < BW_T / 16; ++c16) {
+                bf16x8 pb, sb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pb[i] = (__bf16)pv[c16 * 8 + i];
+                    sb[i] = (__bf16)sacc[c16 * 8 + i];
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int e = (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8;
+                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gt + e);
+                    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + e);
+                    vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, vacc[db], 0, 0, 0);
+                    kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, kacc[db], 0, 0, 0);
+                }
+            }
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);
+            store(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    if (mykey < N) {
+        // lane = key row; entry r of block db = dim 32db + 8(r/4) + 4hi + r%4
+        if (dk32 == nullptr) {
+            uint16_t* krow = dk + (((size_t)b * Hkv + g) * N + mykey) * D;
+            uint16_t* vrow = dv + (((size_t)b * Hkv + g) * N + mykey) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int dim0 = db * 32 + rg * 8 + hi * 4;
+                    const f32x16& ka = kacc[db];
+                    const f32x16& va = vacc[db];
+                    *reinterpret_cast<u32x2*>(krow + dim0) =
+                        u32x2{pack_bf16x2(ka[rg * 4] * scale, ka[rg * 4 + 1] * scale),
+                              pack_bf16x2(ka[rg * 4 + 2] * scale, ka[rg * 4 + 3] * scale)};
+                    *reinterpret_cast<u32x2*>(vrow + dim0) =
+                        u32x2{pack_bf16x2(va[rg * 4], va[rg * 4 + 1]), pack_bf16x2(va[rg * 4 + 2], va[rg * 4 + 3])};
+                }
+        } else {
+            float* krow = dk32 + ((size_t)bh * N + mykey) * D;
+            float* vrow = dv32 + ((size_t)bh * N + mykey) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int dim0 = db * 32 + rg * 8 + hi * 4;
+                    const f32x16& ka = kacc[db];
+                    const f32x16& va = vacc[db];
+                    *reinterpret_cast<f32x4*>(krow + dim0) =
+                        f32x4{ka[rg * 4] * scale, ka[rg * 4 + 1] * scale, ka[rg * 4 + 2] * scale,
+                              ka[rg * 4 + 3] * scale};
+                    *reinterpret_cast<f32x4*>(vrow + dim0) =
+                        f32x4{va[rg * 4], va[rg * 4 + 1], va[rg * 4 + 2], va[rg * 4 + 3]};
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- reduce --
+
+// dk[b, g] = sum over the G query heads of group g of dk32[b, h] (head order),
+// rounded to bf16; the same for dv.  Each thread: 4 consecutive elements.
+__global__ void __launch_bounds__(BW_THREADS)
+bwd_reduce_kernel(const float* __restrict__ dk32, const float* __restrict__ dv32,
+                  uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, long long per_head4,
+                  int G, long long total4) {
+    const long long i = (long long)blockIdx.x * BW_THREADS + threadIdx.x;   // over B*Hkv*N*D/4
+    if (i >= total4) return;
+    const long long bg = i / per_head4, e = i - bg * per_head4;
+    const long long src0 = (bg * G) * per_head4 + e;
+    f32x4 sk = *reinterpret_cast<const f32x4*>(dk32 + src0 * 4);
+    f32x4 sv = *reinterpret_cast<const f32x4*>(dv32 + src0 * 4);
+    for (int j = 1; j < G; ++j) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(dk32 + (src0 + j * per_head4) * 4);
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(dv32 + (src0 + j * per_head4) * 4);
+        sk += a;
+        sv += bb;
+    }
+    *reinterpret_cast<u32x2*>(dk + i * 4) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+    *reinterpret_cast<u32x2*>(dv + i * 4) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
+    const int BH = a.B * a.Hq;
+    const long long rows = (long long)BH * a.N;
+    float* delta = a.workspace;
+    const size_t dsz = bwd_delta_floats(a.B, a.Hq, a.N);
+    const int G = a.Hq / a.Hkv;
+    float* dk32 = G > 1 ? a.workspace + dsz : nullptr;
+    float* dv32 = G > 1 ? dk32 + (size_t)BH * a.N * D : nullptr;
+    const float c = a.scale * kLog2e;
+
+    const long long prep_threads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((prep_threads + BW_THREADS - 1) / BW_THREADS)),
+                       dim3(BW_THREADS), 0, stream, static_cast<const uint16_t*>(a.o),
+                       static_cast<const uint16_t*>(a.dout), delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    const int n_qt = (a.N + PF_BM - 1) / PF_BM;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                       delta, static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, BH, n_qt, c, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                       delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dk32, dv32,
+                       a.Hq, a.Hkv, a.N, BH, n_qt, c, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess || G == 1) return e;
+
+    const long long per_head4 = (long long)a.N * D / 4;
+    const long long total4 = (long long)a.B * a.Hkv * per_head4;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total4 + BW_THREADS - 1) / BW_THREADS)),
+                       dim3(BW_THREADS), 0, stream, dk32, dv32, static_cast<uint16_t*>(a.dk),
+                       static_cast<uint16_t*>(a.dv), per_head4, G, total4);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
+    if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+    return a.causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+}
+
+}  // namespace attn

@@ -100,4 +100,35 @@ struct PagedPrefillArgs {
 
 hipError_t launch_paged_prefill_bf16(const PagedPrefillArgs& a, hipStream_t stream);
 
+// Backward pass.  Workspace: D_i = <do_i, o_i> for every row (fp32, padded to
+// 256 bytes), then, with grouped K/V heads (Hq > Hkv), one fp32 dk and one
+// fp32 dv per query head ([B, Hq, N, d] each) that a last kernel sums per
+// group.
+inline size_t bwd_delta_floats(int B, int Hq, int N) {
+    return (((size_t)B * Hq * N) + 63) & ~(size_t)63;
+}
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+    size_t f = bwd_delta_floats(B, Hq, N);
+    if (Hq != Hkv) f += 2 * (size_t)B * Hq * N * d;
+    return f * sizeof(float);
+}
+
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, N, d;
+    float scale;
+    int causal;
+    float* workspace;
+};
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
+
 }  // namespace attn

@@ -223,6 +223,46 @@ attn_status attn_paged_prefill(const void* q, const void* k_cache, const void* v
                                int T, int max_new, int Hq, int Hkv, int d, int max_blocks,
                                int num_blocks, float scale, attn_dtype dtype, void* stream);
 
+/*
+ * attn_bwd_workspace_size - bytes of device workspace attn_bwd needs (0 on
+ * invalid sizes): 4 * round_up(B*Hq*N, 64) for the per-row D_i, plus, when
+ * Hq > Hkv, 2 * 4 * B*Hq*N*d for one fp32 dk and dv per query head.
+ */
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * attn_bwd - gradients of attn_fwd's output with respect to q, k and v,
+ * recomputing the attention weights from q, k and the saved statistic lse
+ * instead of storing them ("Autoatención, kernels CUDA y FlashAttention",
+ * section 3, recomputation in the backward pass).  For the allowed keys of
+ * row i (as in attn_fwd), p_ij = exp(scale <q_i, k_j> - lse_i) and
+ * D_i = <dout_i, o_i>:
+ *
+ *     dv_j = sum_i p_ij dout_i
+ *     ds_ij = p_ij (<dout_i, v_j> - D_i)
+ *     dq_i = scale sum_j ds_ij k_j,    dk_j = scale sum_i ds_ij q_i
+ *
+ * with dk, dv of a kv head summed over the query heads that read it.
+ *
+ *   q, o, dout, dq : [B, Hq, N, d]  bf16 (o as attn_fwd wrote it, dout the
+ *                    upstream gradient of o)
+ *   k, v, dk, dv   : [B, Hkv, N, d] bf16
+ *   lse            : [B, Hq, N] fp32, as attn_fwd wrote it for the same
+ *                    q, k, v, scale and causal flag
+ *   workspace      : at least attn_bwd_workspace_size(...) bytes, 16-byte
+ *                    aligned; contents on entry ignored
+ *
+ * Accumulation is fp32; the weights and ds enter the matrix products as
+ * bf16; outputs are rounded to nearest-even.  No atomics: results are
+ * deterministic.  Supported: BF16; d = 64 or 128; the other limits of
+ * attn_fwd.  dq, dk, dv and the workspace must not overlap the inputs or
+ * each other.  Errors as for attn_fwd.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                     int d, float scale, int causal, attn_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_string(attn_status s);
 

@@ -41,7 +41,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-                            "attn_kv_append", "attn_paged_prefill",
+                            "attn_kv_append", "attn_paged_prefill", "attn_bwd",
+                            "attn_bwd_workspace_size",
                             "attn_status_string", "attn_last_error", "attn_abi_version"])
 
 
@@ -168,6 +169,35 @@ def test_paged_prefill_with_no_rows_launches_nothing(lib):
     assert ppf(lib, T=0) == OK and ppf(lib, max_new=0) == OK
 
 
+def bwd(lib, q=A, k=A + 16 * MB, v=A + 32 * MB, o=A + 48 * MB, lse=A + 64 * MB, do=A + 80 * MB,
+        dq=A + 96 * MB, dk=A + 112 * MB, dv=A + 128 * MB, B=1, Hq=4, Hkv=2, N=128, d=128, scale=0.1,
+        causal=1, dtype=BF16, ws=A + 144 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_bwd_workspace_size(B, Hq, Hkv, N, d)
+    return lib.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, dtype, ws,
+                        ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(lse=0), INVALID), (dict(do=0), INVALID), (dict(dv=0), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(causal=3), INVALID),
+    (dict(scale=math.inf), INVALID), (dict(dtype=F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(N=1 << 24), UNSUPPORTED), (dict(ws=0), INVALID), (dict(ws_bytes=64), INVALID),
+    (dict(q=A + 8), INVALID), (dict(lse=A + 64 * MB + 2), INVALID), (dict(ws=A + 144 * MB + 4), INVALID),
+    (dict(dq=A), INVALID), (dict(dk=A + 96 * MB), INVALID), (dict(ws=A + 128 * MB), INVALID),
+])
+def test_bwd_rejects_before_any_launch(lib, kw, status):
+    assert bwd(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_bwd_workspace_size(lib):
+    # per-row D (rounded up to 64 floats), plus fp32 dk, dv per query head when grouped
+    assert lib.attn_bwd_workspace_size(1, 4, 4, 100, 128) == 4 * 448      # 400 rows -> 448
+    assert lib.attn_bwd_workspace_size(2, 12, 2, 8192, 128) == 4 * (2 * 12 * 8192 + 2 * 2 * 12 * 8192 * 128)
+    assert lib.attn_bwd_workspace_size(1, 6, 4, 10, 64) == 0
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd") or torch.cuda.is_available()
 
@@ -178,6 +208,7 @@ def test_no_device_status(lib):
     assert dec(lib) == NO_DEVICE
     assert app(lib) == NO_DEVICE
     assert ppf(lib) == NO_DEVICE
+    assert bwd(lib) == NO_DEVICE
 
 
 def test_binding_rejects_host_tensors():
