@@ -15,8 +15,8 @@ with HIP events on the launch stream); the decode's GB/s (algorithmic bytes
 over its average time) is reported beside it.  The steps either side of
 decode are timed after the main loop, on the same 64-sequence cache: the
 chunked prefill of 256 new rows per sequence (attn_paged_prefill) and the
-append of those rows' keys and values (attn_kv_append).  Prints ONE JSON
-line.
+append of those rows' keys and values (attn_kv_append); and the backward
+pass (attn_bwd) of the prefill workload.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -174,7 +174,7 @@ def main(argv=None):
 
     import torch
     from exact_tiled_self_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
-    from exact_tiled_self_amd import attn_kv_append, attn_paged_prefill
+    from exact_tiled_self_amd import attn_bwd, attn_bwd_workspace_size, attn_kv_append, attn_paged_prefill
     from exact_tiled_self_amd import _lib
     from exact_tiled_self_amd.inputs import (CHUNK_NEW, DENSE_CONFIGS, PAGED_CONFIG, chunked_inputs,
                                              dense_inputs)
@@ -293,6 +293,19 @@ def main(argv=None):
     ap_ms = timed(append, K)
     del kc2, vc2
 
+    # the backward pass of the prefill workload (upstream gradient N(0,1), seed 100)
+    g_np = np.random.default_rng(100).standard_normal((pcfg.B, pcfg.Hq, pcfg.N, pcfg.d), dtype=np.float32)
+    dod = torch.from_numpy(g_np).to(torch.bfloat16).to(dev)
+    dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    bws = torch.empty(attn_bwd_workspace_size(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.N, pcfg.d), dtype=torch.uint8,
+                      device=dev)
+
+    def backward():
+        attn_bwd(qd, kd, vd, o, lse, dod, scale=pcfg.scale, causal=True, dq=dqd, dk=dkd, dv=dvd,
+                 workspace=bws, stream=stream)
+
+    bw_ms = timed(backward, max(10, K // 5))
+
     # parity spot check on the benchmarked buffers (sampled rows / sequences)
     from oracle import exact as OA
     rows = np.array([0, 1, 4095, 8190, 8191])
@@ -312,6 +325,11 @@ def main(argv=None):
                               p["v_cache"].float().numpy(), p["block_table"].numpy()[cs:cs + 1],
                               p["ctx_lens"].numpy()[cs:cs + 1], [0, st[cs + 1] - st[cs]], 16, dcfg.scale)
     cerr = float(np.abs(oc[st[cs]:st[cs + 1]].double().cpu().numpy() - ro).max())
+    # backward: dq rows sampled against the oracle's per-head gradients of one head pair
+    from oracle import backward as OB
+    hs = [0, 6]
+    bq = OB.attention_bwd(qn[:, hs], kn, vn, dod[:, hs].double().cpu().numpy(), pcfg.scale, True)[0]
+    berr = float(np.abs(dqd[:, hs].double().cpu().numpy() - bq).max() / max(1.0, np.abs(bq).max()))
 
     clocks = None if args.no_clocks else read_clocks()
 
@@ -325,6 +343,8 @@ def main(argv=None):
     cf, cb = chunked_flops(p, dcfg), chunked_bytes(p, dcfg)
     ch_avg, ap_avg = float(np.mean(ch_ms)), float(np.mean(ap_ms))
     ab = append_bytes(p, dcfg)
+    bw_avg = float(np.mean(bw_ms))
+    bf = 2.5 * pf                       # five products (S recomputed, dP, dV, dK, dQ) against two
 
     out = {
         "metric": METRIC,
@@ -385,8 +405,18 @@ def main(argv=None):
             "min_us": round(min(ap_ms) * 1e3, 2), "bytes": ab, "kernel": "kv_append_kernel",
             "traffic": profiled_traffic("kv_append_bf16_d128_s64_c256",
                                         ["kv_append.hip", "common.h", "internal.h"])},
+        "backward": {
+            "workload": "gqa_causal_t8192 (dout N(0,1), seed 100)",
+            "value": round(bf / (bw_avg * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "frac_mfma": round(bf / (bw_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_us": round(bw_avg * 1e3, 2), "median_us": round(float(np.median(bw_ms)) * 1e3, 2),
+            "min_us": round(min(bw_ms) * 1e3, 2), "flops": bf,
+            "kernels": "bwd_prep + bwd_dq + bwd_kv (dV pass) + bwd_kv (dK pass) + bwd_reduce",
+            "traffic": profiled_traffic("backward_bf16_d128_causal_gqa_t8192",
+                                        ["backward_bf16.hip", "prefill_tile.h", "common.h", "internal.h"])},
         "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,
-                   "chunked_prefill_sampled_max_abs": cerr, "tolerance": 2e-2},
+                   "chunked_prefill_sampled_max_abs": cerr, "tolerance": 2e-2,
+                   "backward_dq_heads_0_6_rel_max": berr, "backward_tolerance_rel": 2e-2},
         "wall_s_timed": round(wall, 3),
         "clocks_after_timing": clocks,
         "library": _lib.library_path(),

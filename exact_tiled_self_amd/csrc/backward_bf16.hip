@@ -10,7 +10,7 @@
 //   dv_j = sum_i p_ij do_i,   dp_ij = <do_i, v_j>,   ds_ij = p_ij (dp_ij - D_i)
 //   dq_i = scale * sum_j ds_ij k_j,   dk_j = scale * sum_i ds_ij q_i
 //
-// Four kernels, none with atomics (results are deterministic):
+// Five kernels, none with atomics (results are deterministic):
 //   * bwd_prep: D_i from o and do (fp32), into the workspace.
 //   * bwd_dq: 4 waves x 32 query rows, key tiles of 32; per tile S^T = K Q^T
 //     and dP^T = V dO^T on MFMA (a lane owns one query row, so lse_i and D_i
@@ -18,12 +18,12 @@
 //     dS^T taken straight from the accumulators as the B operand.  K and V
 //     are staged row-major (XOR-swizzled 16-byte chunks) and K^T transposed
 //     with the accumulator key order (bits 2 and 3 of the key swapped).
-//   * bwd_dkdv: 4 waves x 32 keys, query chunks of 32; per chunk S = Q K^T
-//     and dP = dO V^T (a lane owns one key; its K and V rows stay in
-//     registers), P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS.
-//     Q and dO are staged row-major and transposed; lse and D per query go
-//     through LDS.
-//   * bwd_reduce: with grouped K/V heads the dkdv kernel writes one fp32
+//   * bwd_kv (twice): 4 waves x 32 keys, query chunks of 32; a lane owns one
+//     key, its K (and V) rows stay in registers.  The dV pass computes
+//     S = Q K^T, P and dV^T += dO^T P; the dK pass S, dP = dO V^T,
+//     dS = P (dP - D) and dK^T += Q^T dS.  lse and D per query go through
+//     LDS.
+//   * bwd_reduce: with grouped K/V heads the two passes write one fp32
 //     dk, dv per query head into the workspace and this kernel sums each
 //     group in head order into the bf16 outputs.
 // Causal tiles entirely outside the triangle are never visited; the heaviest
@@ -36,7 +36,7 @@ namespace attn {
 namespace {
 
 constexpr int BW_THREADS = 256;
-constexpr int BW_T = 32;                  // keys per dq tile / queries per dkdv chunk
+constexpr int BW_T = 32;                  // keys per dq tile / queries per dk, dv chunk
 constexpr float kInf = __builtin_inff();
 
 // One staged 32 x D tile: row-major with XOR-swizzled 16-byte chunks, and
@@ -66,6 +66,21 @@ __device__ __forceinline__ void bw_store_both(uint16_t* rm, uint16_t* tr, const 
     *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0, vdc)) = x[0];
     *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0 + 1, vdc)) = x[1];
     const int pos = swap23(r0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        *reinterpret_cast<uint32_t*>(tr + (vdc * 8 + j) * L::TSTR + pos) =
+            __builtin_amdgcn_perm(x[1][w], x[0][w], sel);
+    }
+}
+
+// The same rows, transposed only.
+template <int D>
+__device__ __forceinline__ void bw_store_tr(uint16_t* tr, const u32x4* x, int t) {
+    using L = BwTile<D>;
+    const int kq = t % 16, vdc = t / 16;
+    const int pos = swap23(2 * kq);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int w = j >> 1;
@@ -258,19 +273,38 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
 }
 
-// ------------------------------------------------------------------ dkdv --
+// ------------------------------------------------------------- dk and dv --
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                const float* __restrict__ lse, const float* __restrict__ delta,
-                uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dk32,
-                float* __restrict__ dv32, int Hq, int Hkv, int N, int BH, int n_ktiles, float c,
-                float scale) {
+// One pass per gradient (MODE = kDV or kDK): a wave owns 32 keys, whose K
+// (and for dK, V) rows stay in registers as B operands; query chunks of 32
+// are staged in LDS.  Splitting dV from dK recomputes S once more but keeps
+// each pass within two waves per SIMD (a fused pass would hold both 32-key
+// accumulator tiles, K and V, and spill).
+//   dV pass: S = Q K^T, P = 2^(c s - lse2), dV^T += dO^T P  (Q row-major, dO^T)
+//   dK pass: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS (Q both ways, dO)
+constexpr int kDV = 0, kDK = 1;
+
+template <int D, int MODE>
+struct KvStage {
     using L = BwTile<D>;
-    constexpr int STAGE = 2 * (L::ROW + L::TRN) + 2 * BW_T * 2;   // Q, dO both ways + lse2, D
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    // element offsets inside one stage
+    static constexpr int QRM = 0;                                   // Q row-major
+    static constexpr int SEC = L::ROW;                              // dO^T (dV) or dO row-major (dK)
+    static constexpr int QTR = SEC + (MODE == kDV ? L::TRN : L::ROW);   // Q^T (dK only)
+    static constexpr int STATS = QTR + (MODE == kDV ? 0 : L::TRN);  // lse2 [32], D [32] as floats
+    static constexpr int SIZE = STATS + 2 * BW_T * 2;
+};
+
+template <int D, bool CAUSAL, int MODE>
+__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+              const float* __restrict__ lse, const float* __restrict__ delta,
+              uint16_t* __restrict__ out, float* __restrict__ out32, int Hq, int Hkv, int N, int BH,
+              float c, float scale) {
+    using L = BwTile<D>;
+    using St = KvStage<D, MODE>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * St::SIZE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -288,86 +322,101 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(dout + (size_t)bh * N * D, head_bytes);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
-    (void)n_ktiles;
 
     const int key0 = kt * PF_BM;
     const int wkey0 = key0 + wave * 32;
     const int mykey = wkey0 + l32;
     const bool wave_active = wkey0 < N;
 
-    // This lane's key row of K and V as B operands (dims 16*ks + 8*hi .. +7).
-    bf16x8 kf[D / 16], vf[D / 16];
+    // This lane's key row of K (and V) as B operands (dims 16*ks + 8*hi .. +7).
+    bf16x8 kf[D / 16], vf[MODE == kDK ? D / 16 : 1];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = (uint32_t)(mykey * D + ks * 16 + hi * 8) * 2;
         kf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(krs, off));
-        vf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(vrs, off));
+        if constexpr (MODE == kDK) vf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(vrs, off));
     }
 
-    // Query chunks: all of them, or (causal) those with a query >= key0.
+    // Query chunks: all, or (causal) those with a query >= key0.
     const int c_first = CAUSAL ? key0 / BW_T : 0;
     const int n_c = (N + BW_T - 1) / BW_T;
 
+    // Staging.  The tensor needed both ways (dV: dO, only transposed; dK: Q)
+    // goes through registers: thread t < NST holds rows 2*(t%16) + {0,1},
+    // dims 8*(t/16) .. +7.  The one needed row-major only (dV: Q, dK: dO)
+    // goes straight to LDS, chunk p = i * 256 + tid of the tile.
+    constexpr int RINST = L::ROW / 8 / BW_THREADS;
     const bool st = tid < L::NST;
     const uint32_t soff = (uint32_t)((2 * (tid % 16)) * D + (tid / 16) * 8) * 2;
-    u32x4 qreg[2], greg[2];
+    uint32_t roff[RINST];
+#pragma unroll
+    for (int i = 0; i < RINST; ++i) {
+        const int p = (i * PF_WAVES + wave) * 64 + lane;
+        const int r = p / L::CPR;
+        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
+        roff[i] = (uint32_t)(r * D + cc * 8) * 2;
+    }
+    const __amdgpu_buffer_rsrc_t reg_rs = MODE == kDV ? ors : qrs;   // through registers
+    const __amdgpu_buffer_rsrc_t lds_rs = MODE == kDV ? qrs : ors;   // straight to LDS
+    constexpr int LDS_DST = MODE == kDV ? St::QRM : St::SEC;
+    u32x4 sreg[2];
     float lreg = 0.f, dreg = 0.f;
     const float* lse_h = lse + (size_t)bh * N;
     const float* del_h = delta + (size_t)bh * N;
 
-    auto issue_loads = [&](int cj) {
+    auto issue_loads = [&](int cj, int buf) {
         const uint32_t t0 = (uint32_t)cj * BW_T * D * 2;
+        uint16_t* dst = smem + buf * St::SIZE + LDS_DST;
+#pragma unroll
+        for (int i = 0; i < RINST; ++i)
+            buf_ld16_lds(lds_rs, dst + (i * PF_WAVES + wave) * 64 * 8, t0 + roff[i]);
         if (st) {
-            qreg[0] = buf_ld16(qrs, t0 + soff);
-            qreg[1] = buf_ld16(qrs, t0 + soff + D * 2);
-            greg[0] = buf_ld16(ors, t0 + soff);
-            greg[1] = buf_ld16(ors, t0 + soff + D * 2);
+            sreg[0] = buf_ld16(reg_rs, t0 + soff);
+            sreg[1] = buf_ld16(reg_rs, t0 + soff + D * 2);
         }
         if (tid < BW_T) {
             const int qi = cj * BW_T + tid;
             lreg = qi < N ? lse_h[qi] * kLog2e : kInf;
-            dreg = qi < N ? del_h[qi] : 0.f;
+            if constexpr (MODE == kDK) dreg = qi < N ? del_h[qi] : 0.f;
         }
     };
     auto store = [&](int buf) {
-        uint16_t* base = smem + buf * STAGE;
+        uint16_t* base = smem + buf * St::SIZE;
         if (st) {
-            bw_store_both<D>(base, base + 2 * L::ROW, qreg, tid);
-            bw_store_both<D>(base + L::ROW, base + 2 * L::ROW + L::TRN, greg, tid);
+            if constexpr (MODE == kDV) {
+                bw_store_tr<D>(base + St::SEC, sreg, tid);
+            } else {
+                bw_store_both<D>(base + St::QRM, base + St::QTR, sreg, tid);
+            }
         }
         if (tid < BW_T) {
-            float* stats = reinterpret_cast<float*>(base + 2 * (L::ROW + L::TRN));
+            float* stats = reinterpret_cast<float*>(base + St::STATS);
             stats[tid] = lreg;
             stats[BW_T + tid] = dreg;
         }
     };
 
-    f32x16 kacc[D / 32], vacc[D / 32];
+    f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { kacc[db][r] = 0.f; vacc[db][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    if (c_first < n_c) {
-        issue_loads(c_first);
-        __builtin_amdgcn_s_waitcnt(0);
-        store(0);
-    }
+    issue_loads(c_first, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    store(0);
     __syncthreads();
 
     for (int cj = c_first; cj < n_c; ++cj) {
         const int buf = (cj - c_first) & 1;
         const bool more = cj + 1 < n_c;
-        if (more) issue_loads(cj + 1);
+        if (more) issue_loads(cj + 1, buf ^ 1);
         const int qc = cj * BW_T;
         // skip a chunk whose queries all precede this wave's keys
         if (wave_active && (!CAUSAL || qc + BW_T - 1 >= wkey0)) {
-            const uint16_t* Qs = smem + buf * STAGE;
-            const uint16_t* Gs = Qs + L::ROW;
-            const uint16_t* Qt = Qs + 2 * L::ROW;
-            const uint16_t* Gt = Qt + L::TRN;
-            const float* stats = reinterpret_cast<const float*>(Qs + 2 * (L::ROW + L::TRN));
-            // S = Q K^T and dP = dO V^T: lane = key, entry r = query
+            const uint16_t* base = smem + buf * St::SIZE;
+            const float* stats = reinterpret_cast<const float*>(base + St::STATS);
+            // S = Q K^T (and dP = dO V^T): lane = key, entry r = query
             // qc + 8(r/4) + 4hi + r%4.
             f32x16 sacc, pacc;
 #pragma unroll
@@ -375,18 +424,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 const int e = bw_rm<D>(l32, ks * 2 + hi);
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + e);
-                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + e);
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(base + St::QRM + e);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
+                if constexpr (MODE == kDK) {
+                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(base + St::SEC + e);
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
+                }
             }
             const bool need_mask = (qc + BW_T > N) || (mykey >= N) ||
                                    (CAUSAL && qc < wkey0 + 31);
-            f32x16 pv;
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + BW_T + 8 * rg + 4 * hi);
+                f32x4 d4;
+                if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + BW_T + 8 * rg + 4 * hi);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rg * 4 + i;
@@ -396,26 +447,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const bool ok = qi < N && mykey < N && (!CAUSAL || mykey <= qi);
                         p = ok ? p : 0.f;
                     }
-                    pv[r] = p;
-                    sacc[r] = p * (pacc[r] - d4[i]);
+                    if constexpr (MODE == kDK) p *= pacc[r] - d4[i];
+                    sacc[r] = p;
                 }
             }
-            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
+            // dV^T += dO^T P, or dK^T += Q^T dS: 16 queries per MFMA.
+            const uint16_t* At = base + (MODE == kDV ? St::SEC : St::QTR);
 #pragma unroll
             for (int c16 = 0; c16 < BW_T / 16; ++c16) {
-                bf16x8 pb, sb;
+                bf16x8 pb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    pb[i] = (__bf16)pv[c16 * 8 + i];
-                    sb[i] = (__bf16)sacc[c16 * 8 + i];
-                }
+                for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[c16 * 8 + i];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int e = (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8;
-                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gt + e);
-                    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + e);
-                    vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, vacc[db], 0, 0, 0);
-                    kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, kacc[db], 0, 0, 0);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        At + (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
                 }
             }
         }
@@ -428,37 +475,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     if (mykey < N) {
         // lane = key row; entry r of block db = dim 32db + 8(r/4) + 4hi + r%4
-        if (dk32 == nullptr) {
-            uint16_t* krow = dk + (((size_t)b * Hkv + g) * N + mykey) * D;
-            uint16_t* vrow = dv + (((size_t)b * Hkv + g) * N + mykey) * D;
+        const float f = MODE == kDK ? scale : 1.f;
+        if (out32 == nullptr) {
+            uint16_t* row = out + (((size_t)b * Hkv + g) * N + mykey) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int dim0 = db * 32 + rg * 8 + hi * 4;
-                    const f32x16& ka = kacc[db];
-                    const f32x16& va = vacc[db];
-                    *reinterpret_cast<u32x2*>(krow + dim0) =
-                        u32x2{pack_bf16x2(ka[rg * 4] * scale, ka[rg * 4 + 1] * scale),
-                              pack_bf16x2(ka[rg * 4 + 2] * scale, ka[rg * 4 + 3] * scale)};
-                    *reinterpret_cast<u32x2*>(vrow + dim0) =
-                        u32x2{pack_bf16x2(va[rg * 4], va[rg * 4 + 1]), pack_bf16x2(va[rg * 4 + 2], va[rg * 4 + 3])};
+                    *reinterpret_cast<u32x2*>(row + dim0) =
+                        u32x2{pack_bf16x2(acc[db][rg * 4] * f, acc[db][rg * 4 + 1] * f),
+                              pack_bf16x2(acc[db][rg * 4 + 2] * f, acc[db][rg * 4 + 3] * f)};
                 }
         } else {
-            float* krow = dk32 + ((size_t)bh * N + mykey) * D;
-            float* vrow = dv32 + ((size_t)bh * N + mykey) * D;
+            float* row = out32 + ((size_t)bh * N + mykey) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int dim0 = db * 32 + rg * 8 + hi * 4;
-                    const f32x16& ka = kacc[db];
-                    const f32x16& va = vacc[db];
-                    *reinterpret_cast<f32x4*>(krow + dim0) =
-                        f32x4{ka[rg * 4] * scale, ka[rg * 4 + 1] * scale, ka[rg * 4 + 2] * scale,
-                              ka[rg * 4 + 3] * scale};
-                    *reinterpret_cast<f32x4*>(vrow + dim0) =
-                        f32x4{va[rg * 4], va[rg * 4 + 1], va[rg * 4 + 2], va[rg * 4 + 3]};
+                    *reinterpret_cast<f32x4*>(row + dim0) =
+                        f32x4{acc[db][rg * 4] * f, acc[db][rg * 4 + 1] * f, acc[db][rg * 4 + 2] * f,
+                              acc[db][rg * 4 + 3] * f};
                 }
         }
     }
@@ -514,11 +552,16 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDV>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
-                       delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dk32, dv32,
-                       a.Hq, a.Hkv, a.N, BH, n_qt, c, a.scale);
+                       delta, static_cast<uint16_t*>(a.dv), dv32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDK>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                       delta, static_cast<uint16_t*>(a.dk), dk32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess || G == 1) return e;
 
