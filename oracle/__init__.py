@@ -18,6 +18,8 @@ kvcache     appending new tokens' keys and values to a paged KV cache,
             one token at a time through the block table
 backward    the gradients dq, dk, dv of the exact attention (chain rule
             through o = P V and the softmax, weights recomputed from q, k)
+fusion      residual add + RMSNorm and the SwiGLU activation (silu(g) * u),
+            the memory-bound fusions around attention in a layer
 
 Sources (web pages; cited by title and section):
   [AT]  "Autoatención, kernels CUDA y FlashAttention", section 1 (how
@@ -44,3 +46,4 @@ from .recurrence import (  # noqa: F401
 )
 from .kvcache import append_paged  # noqa: F401
 from .backward import attention_bwd  # noqa: F401
+from .fusion import add_rmsnorm, swiglu  # noqa: F401
