@@ -19,7 +19,8 @@ import torch
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-           "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
+           "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size",
+           "attn_add_rmsnorm", "attn_swiglu", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_BF16"]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_NO_DEVICE, ATTN_ERR_LAUNCH = range(5)
@@ -72,6 +73,10 @@ def raw_library():
         lib.attn_bwd.restype = ci
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp,
                                  sz, vp]
+        lib.attn_add_rmsnorm.restype = ci
+        lib.attn_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ci, ci, cf, ci, vp]
+        lib.attn_swiglu.restype = ci
+        lib.attn_swiglu.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ci]
         lib.attn_last_error.restype = ctypes.c_char_p
@@ -268,3 +273,46 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, *, dq=None, dk=Non
         workspace.numel() * workspace.element_size(), _stream_ptr(q.device, stream))
     _check(st)
     return dq, dk, dv
+
+
+def attn_add_rmsnorm(x, residual, weight, eps=1e-6, *, out=None, residual_out=None, stream=None):
+    """Returns (out, residual_out): residual_out = bf16(x + residual) and
+    out = RMSNorm(residual_out) * weight.  x, residual: [T, D] bf16; weight
+    [D].  Pass residual_out=residual to update the residual in place."""
+    if x.dim() != 2 or residual.shape != x.shape or weight.dim() != 1 or weight.shape[0] != x.shape[1]:
+        raise ValueError("x, residual must be [T, D] and weight [D]")
+    if not (x.dtype == residual.dtype == weight.dtype) or x.dtype not in _DTYPE:
+        raise ValueError("x, residual and weight must share dtype")
+    out = torch.empty_like(x) if out is None else out
+    residual_out = torch.empty_like(x) if residual_out is None else residual_out
+    T, D = x.shape
+    st = raw_library().attn_add_rmsnorm(_dev(x, "x"), _dev(residual, "residual"), _dev(weight, "weight"),
+                                        _dev(out, "out"), _dev(residual_out, "residual_out"), T, D,
+                                        float(eps), _DTYPE[x.dtype], _stream_ptr(x.device, stream))
+    _check(st)
+    return out, residual_out
+
+
+def attn_swiglu(gate, up=None, *, out=None, stream=None):
+    """silu(gate) * up.  With up=None, gate is one merged [T, 2F] projection
+    output whose first F columns are the gate and last F the up half."""
+    if gate.dim() != 2 or gate.dtype not in _DTYPE:
+        raise ValueError("gate must be a 2-D tensor")
+    if up is None:
+        T, F2 = gate.shape
+        if F2 % 2:
+            raise ValueError("a merged gate/up tensor needs an even width")
+        F, ld_in = F2 // 2, F2
+        g_ptr = _dev(gate, "gate")
+        u_ptr = g_ptr + F * gate.element_size()
+    else:
+        if up.shape != gate.shape or up.dtype != gate.dtype:
+            raise ValueError("gate and up must match")
+        T, F = gate.shape
+        ld_in = F
+        g_ptr, u_ptr = _dev(gate, "gate"), _dev(up, "up")
+    out = torch.empty((T, F), dtype=gate.dtype, device=gate.device) if out is None else out
+    st = raw_library().attn_swiglu(g_ptr, u_ptr, _dev(out, "out"), T, F, ld_in, F, _DTYPE[gate.dtype],
+                                   _stream_ptr(gate.device, stream))
+    _check(st)
+    return out

@@ -23,7 +23,7 @@ LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "prefill_paged.hip",
-           "kv_append.hip", "backward_bf16.hip"]
+           "kv_append.hip", "backward_bf16.hip", "fusion.hip"]
 
 # Device-code flags: gfx950 only; packed fp32 instructions disabled.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -348,4 +348,57 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     return launch_status(attn::launch_backward_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_add_rmsnorm(const void* x, const void* residual, const void* weight, void* out,
+                             void* residual_out, int T, int D, float eps, attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    if (!x || !residual || !weight || !out || !residual_out)
+        return fail(ATTN_ERR_INVALID_ARG, "x, residual, weight, out and residual_out must be non-null");
+    if (T < 0 || D < 1) return fail(ATTN_ERR_INVALID_ARG, "T must be >= 0 and D >= 1");
+    if (!isfinite(eps) || eps < 0.f) return fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "add_rmsnorm supports bf16 only");
+    if (D % 8 != 0 || D > 8192) return fail(ATTN_ERR_UNSUPPORTED, "D must be a multiple of 8, at most 8192");
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
+        !aligned(residual_out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "all pointers must be 16-byte aligned");
+    const size_t rb = (size_t)T * D * 2, wb = (size_t)D * 2;
+    if (overlap(out, rb, x, rb) || overlap(out, rb, residual, rb) || overlap(out, rb, weight, wb) ||
+        overlap(out, rb, residual_out, rb))
+        return fail(ATTN_ERR_INVALID_ARG, "out must not overlap the inputs or residual_out");
+    if ((residual_out != residual && overlap(residual_out, rb, residual, rb)) ||
+        overlap(residual_out, rb, x, rb) || overlap(residual_out, rb, weight, wb))
+        return fail(ATTN_ERR_INVALID_ARG, "residual_out must be residual itself or overlap no input");
+    if (T == 0) return ATTN_OK;
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+    attn::AddRmsNormArgs a;
+    a.x = x; a.residual = residual; a.weight = weight; a.out = out; a.residual_out = residual_out;
+    a.T = T; a.D = D; a.eps = eps;
+    return launch_status(attn::launch_add_rmsnorm_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_swiglu(const void* gate, const void* up, void* out, int T, int F, int ld_in, int ld_out,
+                        attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    if (!gate || !up || !out) return fail(ATTN_ERR_INVALID_ARG, "gate, up and out must be non-null");
+    if (T < 0 || F < 1) return fail(ATTN_ERR_INVALID_ARG, "T must be >= 0 and F >= 1");
+    if (ld_in < F || ld_out < F) return fail(ATTN_ERR_INVALID_ARG, "row strides must be >= F");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "swiglu supports bf16 only");
+    if (F % 8 != 0 || ld_in % 8 != 0 || ld_out % 8 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "F and the row strides must be multiples of 8");
+    if ((long long)T * (F / 8) >= (1LL << 38)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "gate, up and out must be 16-byte aligned");
+    const size_t ib = T ? ((size_t)(T - 1) * ld_in + F) * 2 : 0, ob = T ? ((size_t)(T - 1) * ld_out + F) * 2 : 0;
+    if (overlap(out, ob, gate, ib) || overlap(out, ob, up, ib))
+        return fail(ATTN_ERR_INVALID_ARG, "out must not overlap gate or up");
+    if (T == 0) return ATTN_OK;
+
+    attn_status st = check_device();
+    if (st != ATTN_OK) return st;
+    attn::SwigluArgs a;
+    a.gate = gate; a.up = up; a.out = out; a.T = T; a.F = F; a.ld_in = ld_in; a.ld_out = ld_out;
+    return launch_status(attn::launch_swiglu_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

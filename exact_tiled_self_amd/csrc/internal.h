@@ -131,4 +131,27 @@ struct BackwardArgs {
 
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
 
+// Residual add + RMSNorm over [T, D] rows (bf16).
+struct AddRmsNormArgs {
+    const void* x;
+    const void* residual;
+    const void* weight;
+    void* out;
+    void* residual_out;   // may be residual itself
+    int T, D;
+    float eps;
+};
+
+hipError_t launch_add_rmsnorm_bf16(const AddRmsNormArgs& a, hipStream_t stream);
+
+// silu(gate) * up over [T, F] (bf16), rows of gate and up ld_in apart.
+struct SwigluArgs {
+    const void* gate;
+    const void* up;
+    void* out;
+    int T, F, ld_in, ld_out;
+};
+
+hipError_t launch_swiglu_bf16(const SwigluArgs& a, hipStream_t stream);
+
 }  // namespace attn

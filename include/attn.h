@@ -263,6 +263,43 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int d, float scale, int causal, attn_dtype dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * attn_add_rmsnorm - residual add fused with RMSNorm ("Kernels de atención
+ * rápida y fusión de operadores", section "Fusión de operadores": adding a
+ * residual connection followed by an RMSNorm is one of the common fusions).
+ * For each of the T rows of D elements:
+ *
+ *     residual_out = bf16(x + residual)                    (the new residual stream)
+ *     out_i = residual_out_i / sqrt(mean_j residual_out_j^2 + eps) * weight_i
+ *
+ * in fp32, out rounded to nearest-even; the norm reads the residual as
+ * stored (bf16), so the result equals an add kernel followed by a norm
+ * kernel.  x, residual, out, residual_out: [T, D] bf16 row-major; weight:
+ * [D] bf16.  residual_out may be residual itself (in-place update); out
+ * overlaps nothing.  Supported: BF16; D a multiple of 8, at most 8192;
+ * T >= 0 (0: nothing to do); eps finite and >= 0; 16-byte aligned pointers.
+ */
+attn_status attn_add_rmsnorm(const void* x, const void* residual, const void* weight, void* out,
+                             void* residual_out, int T, int D, float eps, attn_dtype dtype,
+                             void* stream);
+
+/*
+ * attn_swiglu - the SwiGLU block's activation fused into one pass (same
+ * page and section: the block runs a SiLU kernel and an elementwise-multiply
+ * kernel between its projections): out[t][f] = silu(gate[t][f]) * up[t][f],
+ * silu(g) = g / (1 + e^-g), in fp32, rounded to nearest-even.
+ *
+ *   gate, up : row t at gate + t * ld_in, up + t * ld_in (F elements each):
+ *              two [T, F] tensors (ld_in = F), or the halves of one merged
+ *              [T, 2F] projection output (up = gate + F, ld_in = 2F)
+ *   out      : row t at out + t * ld_out, F elements
+ *
+ * Supported: BF16; F and the strides multiples of 8; strides >= F; T >= 0;
+ * 16-byte aligned pointers; out overlaps neither input.
+ */
+attn_status attn_swiglu(const void* gate, const void* up, void* out, int T, int F, int ld_in,
+                        int ld_out, attn_dtype dtype, void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_string(attn_status s);
 

@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
                             "attn_kv_append", "attn_paged_prefill", "attn_bwd",
-                            "attn_bwd_workspace_size",
+                            "attn_bwd_workspace_size", "attn_add_rmsnorm", "attn_swiglu",
                             "attn_status_string", "attn_last_error", "attn_abi_version"])
 
 
@@ -198,6 +198,45 @@ def test_bwd_workspace_size(lib):
     assert lib.attn_bwd_workspace_size(1, 6, 4, 10, 64) == 0
 
 
+def rms(lib, x=A, r=A + 16 * MB, w=A + 32 * MB, out=A + 48 * MB, rout=A + 64 * MB, T=100, D=1536,
+        eps=1e-6, dtype=BF16):
+    return lib.attn_add_rmsnorm(x, r, w, out, rout, T, D, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), INVALID), (dict(w=0), INVALID), (dict(rout=0), INVALID), (dict(T=-1), INVALID),
+    (dict(D=0), INVALID), (dict(eps=-1.0), INVALID), (dict(eps=math.nan), INVALID),
+    (dict(dtype=F32), UNSUPPORTED), (dict(D=1540), UNSUPPORTED), (dict(D=8200), UNSUPPORTED),
+    (dict(x=A + 8), INVALID), (dict(out=A + 48 * MB + 2), INVALID), (dict(out=A), INVALID),
+    (dict(out=A + 64 * MB), INVALID), (dict(rout=A + 16 * MB + 1024), INVALID), (dict(rout=A + 100), INVALID),
+])
+def test_add_rmsnorm_rejects_before_any_launch(lib, kw, status):
+    assert rms(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_add_rmsnorm_in_place_and_empty(lib):
+    # residual_out == residual is allowed; T = 0 returns OK without a launch
+    assert rms(lib, rout=A + 16 * MB, T=0) == OK
+    assert rms(lib, T=0) == OK
+
+
+def swi(lib, g=A, u=A + 32 * MB, out=A + 64 * MB, T=100, F=8960, ld_in=8960, ld_out=8960, dtype=BF16):
+    return lib.attn_swiglu(g, u, out, T, F, ld_in, ld_out, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=0), INVALID), (dict(out=0), INVALID), (dict(T=-2), INVALID), (dict(F=0), INVALID),
+    (dict(ld_in=100), INVALID), (dict(ld_out=8952), INVALID), (dict(dtype=F32), UNSUPPORTED),
+    (dict(F=8962, ld_in=8968, ld_out=8968), UNSUPPORTED), (dict(ld_in=8964), UNSUPPORTED),
+    (dict(g=A + 4), INVALID), (dict(out=A + 64 * MB + 8), INVALID), (dict(out=A + 1024), INVALID),
+    (dict(out=A + 32 * MB + 4096), INVALID),
+])
+def test_swiglu_rejects_before_any_launch(lib, kw, status):
+    assert swi(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd") or torch.cuda.is_available()
 
@@ -209,6 +248,8 @@ def test_no_device_status(lib):
     assert app(lib) == NO_DEVICE
     assert ppf(lib) == NO_DEVICE
     assert bwd(lib) == NO_DEVICE
+    assert rms(lib) == NO_DEVICE and rms(lib, rout=A + 16 * MB) == NO_DEVICE
+    assert swi(lib) == NO_DEVICE
 
 
 def test_binding_rejects_host_tensors():
