@@ -16,7 +16,10 @@ over its average time) is reported beside it.  The steps either side of
 decode are timed after the main loop, on the same 64-sequence cache: the
 chunked prefill of 256 new rows per sequence (attn_paged_prefill) and the
 append of those rows' keys and values (attn_kv_append); and the backward
-pass (attn_bwd) of the prefill workload.  Prints ONE JSON line.
+pass (attn_bwd) of the prefill workload; and the memory-bound fusions of a
+decoder layer of the same attention shape (8192 tokens, width 1536,
+intermediate 8960): residual add + RMSNorm and the SwiGLU activation.
+Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -175,6 +178,7 @@ def main(argv=None):
     import torch
     from exact_tiled_self_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
     from exact_tiled_self_amd import attn_bwd, attn_bwd_workspace_size, attn_kv_append, attn_paged_prefill
+    from exact_tiled_self_amd import attn_add_rmsnorm, attn_swiglu
     from exact_tiled_self_amd import _lib
     from exact_tiled_self_amd.inputs import (CHUNK_NEW, DENSE_CONFIGS, PAGED_CONFIG, chunked_inputs,
                                              dense_inputs)
@@ -306,6 +310,17 @@ def main(argv=None):
 
     bw_ms = timed(backward, max(10, K // 5))
 
+    # decoder-layer fusions: 8192 tokens, residual width 1536, intermediate 8960
+    T_L, D_L, F_L = 8192, 1536, 8960
+    frng = np.random.default_rng(200)
+    fx = torch.from_numpy(frng.standard_normal((T_L, D_L), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    fr = torch.from_numpy(frng.standard_normal((T_L, D_L), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    fw = torch.from_numpy(1 + 0.1 * frng.standard_normal(D_L).astype(np.float32)).to(torch.bfloat16).to(dev)
+    fgu = torch.from_numpy(frng.standard_normal((T_L, 2 * F_L), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    fo, fro, fa = torch.empty_like(fx), torch.empty_like(fx), torch.empty((T_L, F_L), dtype=torch.bfloat16, device=dev)
+    rms_ms = timed(lambda: attn_add_rmsnorm(fx, fr, fw, 1e-6, out=fo, residual_out=fro, stream=stream), K)
+    swi_ms = timed(lambda: attn_swiglu(fgu, out=fa, stream=stream), K)
+
     # parity spot check on the benchmarked buffers (sampled rows / sequences)
     from oracle import exact as OA
     rows = np.array([0, 1, 4095, 8190, 8191])
@@ -345,6 +360,9 @@ def main(argv=None):
     ab = append_bytes(p, dcfg)
     bw_avg = float(np.mean(bw_ms))
     bf = 2.5 * pf                       # five products (S recomputed, dP, dV, dK, dQ) against two
+    rms_bytes = 4 * T_L * D_L * 2 + D_L * 2          # x, residual read; out, residual written; weight
+    swi_bytes = 3 * T_L * F_L * 2                    # gate, up read; out written
+    rms_avg, swi_avg = float(np.mean(rms_ms)), float(np.mean(swi_ms))
 
     out = {
         "metric": METRIC,
@@ -414,6 +432,18 @@ def main(argv=None):
             "kernels": "bwd_prep + bwd_dq + bwd_kv (dV pass) + bwd_kv (dK pass) + bwd_reduce",
             "traffic": profiled_traffic("backward_bf16_d128_causal_gqa_t8192",
                                         ["backward_bf16.hip", "prefill_tile.h", "common.h", "internal.h"])},
+        "fusion": {
+            "workload": f"decoder layer, {T_L} tokens, width {D_L}, intermediate {F_L}, bf16",
+            "add_rmsnorm": {"value": round(rms_bytes / (rms_avg * 1e-3) / 1e9, 1), "unit": "GB/s",
+                            "frac_hbm": round(rms_bytes / (rms_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                            "avg_us": round(rms_avg * 1e3, 2),
+                            "median_us": round(float(np.median(rms_ms)) * 1e3, 2), "bytes": rms_bytes,
+                            "kernel": "add_rmsnorm_kernel<4>"},
+            "swiglu": {"value": round(swi_bytes / (swi_avg * 1e-3) / 1e9, 1), "unit": "GB/s",
+                       "frac_hbm": round(swi_bytes / (swi_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                       "avg_us": round(swi_avg * 1e3, 2), "median_us": round(float(np.median(swi_ms)) * 1e3, 2),
+                       "bytes": swi_bytes, "kernel": "swiglu_kernel"},
+            "traffic": profiled_traffic("fusion_bf16_t8192_d1536_f8960", ["fusion.hip", "common.h", "internal.h"])},
         "parity": {"prefill_sampled_max_abs": max(errs), "decode_sampled_max_abs": derr,
                    "chunked_prefill_sampled_max_abs": cerr, "tolerance": 2e-2,
                    "backward_dq_heads_0_6_rel_max": berr, "backward_tolerance_rel": 2e-2},
