@@ -283,6 +283,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //   dV pass: S = Q K^T, P = 2^(c s - lse2), dV^T += dO^T P  (Q row-major, dO^T)
 //   dK pass: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS (Q both ways, dO)
 constexpr int kDV = 0, kDK = 1;
+constexpr int kKvRun = 4;           // key tiles of one head kept on one XCD
 
 template <int D, int MODE>
 struct KvStage {
@@ -311,10 +312,16 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int hi = lane >> 5, l32 = lane & 31;
 
     // Work unit (b, h, 128-key tile); with a causal mask the first key tiles
-    // see the most queries and go first.
-    const int wg = blockIdx.x;
-    const int kt = wg / BH;
-    const int bh = wg % BH;
+    // see the most queries and go first.  Units are taken in runs of
+    // kKvRun consecutive key tiles of one head, and workgroup b runs on XCD
+    // b % 8: the j-th workgroup of XCD x takes run (j / R) * 8 + x, so a run's
+    // tiles, which stream the same q and dout rows, share one XCD's L2.
+    constexpr int R = kKvRun;
+    const int xcd = blockIdx.x & (kXcds - 1), jx = blockIdx.x / kXcds;
+    const int u = (jx / R) * (kXcds * R) + xcd * R + jx % R;    // run-major unit index
+    const int run = u / R, kt = (run / BH) * R + u % R;
+    const int bh = run % BH;
+    if (kt * PF_BM >= N) return;
     const int b = bh / Hq, h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
     const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -552,13 +559,16 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDV>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+    const long long kv_units = (long long)((n_qt + kKvRun - 1) / kKvRun) * kKvRun * BH;
+    const long long kv_round = (long long)kXcds * kKvRun;
+    const unsigned kv_grid = (unsigned)((kv_units + kv_round - 1) / kv_round * kv_round);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDV>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
                        delta, static_cast<uint16_t*>(a.dv), dv32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDK>), dim3((unsigned)(BH * n_qt)), dim3(BW_THREADS), 0, stream,
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDK>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
                        delta, static_cast<uint16_t*>(a.dk), dk32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
