@@ -18,15 +18,15 @@
 //     ^ 32, the row sum needs no exchange until the epilogue, and the
 //     rescale of u by e^(m - m') is lane-local.
 //   * O^T = V^T * P^T: P^T comes straight from the score accumulators
-//     (converted to bf16); V^T is read from LDS, where the staging code
-//     stores V transposed with keys 4..7 and 8..11 of every 16-key group
-//     swapped, which is exactly the key order of the accumulator lanes.
+//     (converted to bf16); V^T comes from the row-major V tile through LDS
+//     transpose loads (two per MFMA), which deliver 8 keys of one dim per
+//     lane in the key order of the accumulator lanes.
 //   * K/V tiles are double-buffered in LDS; the loads of tile j+1 are issued
-//     before the MFMA work on tile j.  K goes straight from memory into LDS
-//     (buffer_load ... lds, 16-byte chunks of each row XOR-swizzled so the
-//     operand fetches are free of bank conflicts); V passes through registers
-//     to be stored transposed.  Buffer resources bound every load by the
-//     head's extent, so rows past N read as zero without branches.
+//     before the MFMA work on tile j.  K and V go straight from memory into
+//     LDS (buffer_load ... lds), their 16-byte chunks XOR-swizzled per row so
+//     the operand fetches of each are free of bank conflicts.  Buffer
+//     resources bound every load by the head's extent, so rows past N read
+//     as zero without branches.
 //   * The running maximum is raised lazily: only when a tile's maximum
 //     exceeds it by more than 2^8 in weight does the wave rescale l and u.
 //   * Causal: tiles entirely above the diagonal are never visited, the q
@@ -91,24 +91,27 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
         koff[i] = (uint32_t)(r * D + cc * 8) * 2;
     }
-    // V staging through registers (stored transposed): keys vkg*VKPT + i, dims vdc*8 .. +7.
-    const int vkg = tid % L::VKGROUPS;
-    const int vdc = tid / L::VKGROUPS;
-    const uint32_t voff = (uint32_t)((vkg * L::VKPT) * D + vdc * 8) * 2;
-    u32x4 vreg[L::VKPT];
+    // V staging: the same chunks, straight to LDS, with V's own swizzle.
+    uint32_t voff[L::KINST];
+#pragma unroll
+    for (int i = 0; i < L::KINST; ++i) {
+        const int p = (i * PF_WAVES + wave) * 64 + lane;
+        const int r = p / L::CPR;
+        const int cc = (p % L::CPR) ^ vswz<L::CPR>(r);
+        voff[i] = (uint32_t)(r * D + cc * 8) * 2;
+    }
 
     auto issue_loads = [&](int kt, int buf) {
         const uint32_t t0 = (uint32_t)kt * PF_BN * D * 2;
         uint16_t* Ks = smem + buf * L::BUF;
+        uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
         for (int i = 0; i < L::KINST; ++i)
             buf_ld16_lds(krs, Ks + (i * PF_WAVES + wave) * 64 * 8, t0 + koff[i]);
 #pragma unroll
-        for (int i = 0; i < L::VKPT; ++i) vreg[i] = buf_ld16(vrs, t0 + voff + (uint32_t)(i * D * 2));
+        for (int i = 0; i < L::KINST; ++i)
+            buf_ld16_lds(vrs, Vs + (i * PF_WAVES + wave) * 64 * 8, t0 + voff[i]);
     };
-
-    const int vpos = swap23(vkg * L::VKPT);
-    auto store_v = [&](int buf) { pf_store_vt<D>(smem + buf * L::BUF + L::KELEMS, vreg, vpos, vdc); };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -119,7 +122,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    store_v(0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -134,10 +136,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             pf_tile_step<D, CAUSAL>(Ks, Ks + L::KELEMS, qf, oacc, m_run, l_run, k0, N, myrow,
                                     need_mask, c, hi, l32);
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);     // tile kt+1: K in LDS, V in registers
-            store_v(buf ^ 1);
-        }
+        if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
     }
 

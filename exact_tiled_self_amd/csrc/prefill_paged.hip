@@ -16,7 +16,7 @@
 //
 // Everything else is the dense kernel's tile recurrence (prefill_tile.h):
 // 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in
-// LDS, K loaded straight into LDS, V stored transposed, MFMA 32x32x16 bf16
+// LDS, K and V loaded straight into LDS, MFMA 32x32x16 bf16
 // on S^T = K Q^T and O^T += V^T P^T, lazy rescale of the running maximum.
 // The work units are (query tile, sequence, query head), heads fastest.
 // Sequence lengths vary widely, so the (query tile, sequence) pairs run
@@ -144,22 +144,17 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // Keys 0 .. first + row_end - 1 are needed.
     const int n_kt = (first + row_end - 1) / PF_BN + 1;
 
-    // This wave stages cache block kt*4 + wave of every tile: K chunk p =
-    // (wave * KINST + i) * 64 + lane of the tile (row p / CPR, a row of this
-    // block), V keys 16*wave + VKPT*kq .. + VKPT-1, dims 8*vdc .. +7.
-    uint32_t koff[L::KINST];
+    // This wave stages cache block kt*4 + wave of every tile: chunk p =
+    // (wave * KINST + i) * 64 + lane of the K and of the V tile (row p / CPR,
+    // a row of this block), straight to LDS with each tile's swizzle.
+    uint32_t koff[L::KINST], voff[L::KINST];
 #pragma unroll
     for (int i = 0; i < L::KINST; ++i) {
         const int p = (wave * L::KINST + i) * 64 + lane;
         const int r = p / L::CPR;
-        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
-        koff[i] = (uint32_t)((r - wave * BS) * D + cc * 8) * 2;
+        koff[i] = (uint32_t)((r - wave * BS) * D + ((p % L::CPR) ^ kswz<L::CPR>(r)) * 8) * 2;
+        voff[i] = (uint32_t)((r - wave * BS) * D + ((p % L::CPR) ^ vswz<L::CPR>(r)) * 8) * 2;
     }
-    constexpr int KGRP = BS / L::VKPT;                       // key groups per block
-    const int kq = lane % KGRP, vdc = lane / KGRP;
-    const uint32_t voff = (uint32_t)(kq * L::VKPT * D + vdc * 8) * 2;
-    const int vpos = swap23(wave * BS + kq * L::VKPT);
-    u32x4 vreg[L::VKPT];
     const size_t head_elems = (size_t)BS * D;                 // one (block, kv head) tile
     const int32_t* trow = table + (size_t)s * max_blocks;
     int bad = 0x7fffffff;                                     // lowest block with a bad entry
@@ -183,13 +178,14 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + base, bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + base, bytes);
         uint16_t* Ks = smem + buf * L::BUF;
+        uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
         for (int i = 0; i < L::KINST; ++i)
             buf_ld16_lds(krs, Ks + (wave * L::KINST + i) * 64 * 8, koff[i]);
 #pragma unroll
-        for (int i = 0; i < L::VKPT; ++i) vreg[i] = buf_ld16(vrs, voff + (uint32_t)(i * D * 2));
+        for (int i = 0; i < L::KINST; ++i)
+            buf_ld16_lds(vrs, Vs + (wave * L::KINST + i) * 64 * 8, voff[i]);
     };
-    auto store_v = [&](int buf) { pf_store_vt<D>(smem + buf * L::BUF + L::KELEMS, vreg, vpos, vdc); };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -202,7 +198,6 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    store_v(0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -216,10 +211,7 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             pf_tile_step<D, true>(Ks, Ks + L::KELEMS, qf, oacc, m_run, l_run, k0, ctx, mypos,
                                   need_mask, c, hi, l32);
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);     // tile kt+1: K in LDS, V in registers
-            store_v(buf ^ 1);
-        }
+        if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
     }
 

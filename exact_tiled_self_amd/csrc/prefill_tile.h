@@ -2,8 +2,8 @@
 // and the chunked prefill over a paged cache.
 //
 // A workgroup of 4 waves owns 128 query rows (32 per wave); key tiles of 64
-// keys are staged in LDS: K row-major with 16-byte chunks XOR-swizzled, V
-// transposed.  One call of pf_tile_step advances one wave's 32 rows over one
+// keys are staged in LDS, K and V both row-major with their 16-byte chunks
+// XOR-swizzled (straight from memory, no register staging).  One call of pf_tile_step advances one wave's 32 rows over one
 // staged tile with the online-softmax recurrence ("FlashAttention" notes,
 // section "No basta con promediar los resultados de los bloques"): scores of
 // the tile, new running maximum, rescale of l and u by e^(m - m') when it
@@ -14,9 +14,12 @@
 // one query row per lane (lane % 32) with 16 of its keys per 32-key block,
 // so the row maximum is an in-lane max plus one exchange with lane ^ 32, and
 // the rescale of u is lane-local; O^T += V^T P^T takes P^T straight from the
-// score accumulators.  The V^T layout in LDS stores keys 4..7 and 8..11 of
-// every 16-key group swapped, which is the key order of the accumulator
-// lanes.
+// score accumulators.  The V^T operand is read from the row-major V tile with
+// the LDS transpose load (ds_read_b64_tr_b16): within each 16-lane group it
+// hands lane i the element (i mod 4) of the 8 bytes that lanes i/4, 4 + i/4,
+// 8 + i/4 and 12 + i/4 addressed, i.e. it transposes a 4-row x 16-column
+// block; two of them give a lane 8 keys of one dim, in the key order of the
+// score accumulators.
 #pragma once
 
 #include "common.h"
@@ -30,16 +33,12 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 
 template <int D>
 struct PfLayout {
-    static constexpr int CPR = D / 8;           // 16-byte chunks per K row
-    static constexpr int VSTR = PF_BN + 8;      // bf16 per V^T row in LDS (16-B pad)
+    static constexpr int CPR = D / 8;           // 16-byte chunks per row
     static constexpr int KELEMS = PF_BN * D;    // K tile, rows XOR-swizzled, no pad
-    static constexpr int VELEMS = D * VSTR;
+    static constexpr int VELEMS = PF_BN * D;    // V tile, the same shape
     static constexpr int BUF = KELEMS + VELEMS; // one pipeline stage (bf16 elements)
-    static constexpr int KINST = PF_BN * CPR / PF_THREADS;     // K load-to-LDS per thread
-    static constexpr int VKPT = PF_BN * D / 8 / PF_THREADS;     // keys per thread (V)
-    static constexpr int VKGROUPS = PF_BN / VKPT;
-    static_assert(KINST * PF_THREADS == PF_BN * CPR, "K tile split");
-    static_assert(VKPT == 2 || VKPT == 4, "V staging handles 2 or 4 keys per thread");
+    static constexpr int KINST = PF_BN * CPR / PF_THREADS;     // load-to-LDS per thread per tile
+    static_assert(KINST * PF_THREADS == PF_BN * CPR, "tile split");
 };
 
 // XOR swizzle of the 16-byte chunks of K row r, so that the 16 rows read by
@@ -49,10 +48,34 @@ __device__ __forceinline__ int kswz(int r) {
     return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
-// Position of key x (within a 16-key group) in the V^T layout: bits 2 and 3
-// exchanged.  It is its own inverse.
+// XOR swizzle of the 16-byte chunks of V row r.  A transpose load reads 4
+// consecutive rows x 32 bytes per 16 lanes (and 2 such groups per 32 lanes);
+// shifting rows r..r+3 by 0, 6, 12, 10 chunks puts those reads on distinct
+// banks.
+template <int CPR>
+__device__ __forceinline__ int vswz(int r) {
+    return (0xAC60 >> (4 * (r & 3))) & 15 & (CPR - 1);
+}
+
+// Position of key x (within a 16-key group) in a transposed tile stored with
+// the accumulator key order: bits 2 and 3 exchanged.  It is its own inverse.
 __device__ __forceinline__ int swap23(int x) {
     return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Per-lane element offsets (inside a V tile, before the key-block term) of
+// the two transpose loads that give dims 32*db + (lane % 32), keys
+// 16*c16 + 4*hi + {0..3} and {8..11}; the key-block term (16*c16)*D is added
+// by the caller.  db-dependent: the swizzle mixes the chunk index.
+template <int D>
+__device__ __forceinline__ int pf_vtr_offset(int lane, int db) {
+    constexpr int CPR = D / 8;
+    const int gi = lane >> 4, a = lane & 15;
+    const int row = 4 * (gi >> 1) + (a >> 2);                 // + 16*c16 + 8*rd (multiples of 4)
+    const int chunk = db * 4 + 2 * (gi & 1) + ((a & 3) >> 1);
+    return row * D + ((chunk ^ vswz<CPR>(row)) * 8) + 4 * (a & 1);
 }
 
 // A tile raises the running maximum only when some row's new maximum exceeds
@@ -61,32 +84,12 @@ __device__ __forceinline__ int swap23(int x) {
 // numerator needs no rescale.  u / l is unchanged by the choice of reference.
 constexpr float kLazyLog2 = 8.0f;
 
-// Store the V rows one thread loaded (VKPT keys from key0, dims 8*vdc ..
-// 8*vdc + 7) transposed into the V^T area of an LDS stage; pos = swap23(key0).
-template <int D>
-__device__ __forceinline__ void pf_store_vt(uint16_t* Vt, const u32x4* vreg, int pos, int vdc) {
-    using L = PfLayout<D>;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint16_t* dst = Vt + (vdc * 8 + j) * L::VSTR + pos;
-        if constexpr (L::VKPT == 4) {
-            const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-            const uint32_t hi2 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-            *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi2};
-        } else {
-            *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        }
-    }
-}
-
 // Advance one wave's rows over the tile of keys k0 .. k0 + 63 staged at Ks
-// (K) and Vt (V^T).  Key position `key` is allowed for this lane's row iff
+// (K) and Vs (V, row-major).  Key position `key` is allowed for this lane's row iff
 // key < kend and (when CAUSAL) key <= mypos; `need_mask` must be true
 // whenever some key of the tile fails that test for some row of the wave.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t* Vt, const bf16x8* qf,
+__device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t* Vs, const bf16x8* qf,
                                              f32x16* oacc, float& m_run, float& l_run, int k0,
                                              int kend, int mypos, bool need_mask, float c, int hi,
                                              int l32) {
@@ -165,7 +168,8 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     }
     l_run += lsum;
 
-    // O^T += V^T P^T, 16 keys per MFMA.
+    // O^T += V^T P^T, 16 keys per MFMA; V^T by two transpose loads.
+    const int lane = hi * 32 + l32;
 #pragma unroll
     for (int c16 = 0; c16 < PF_BN / 16; ++c16) {
         const int kb = c16 >> 1, sh = (c16 & 1) * 8;
@@ -174,8 +178,10 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
         for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[kb][sh + i];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                Vt + (db * 32 + l32) * L::VSTR + c16 * 16 + hi * 8);
+            const uint16_t* v0 = Vs + pf_vtr_offset<D>(lane, db) + c16 * 16 * D;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v0));
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v0 + 8 * D));
+            const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
         }
     }
