@@ -39,55 +39,64 @@ constexpr int BW_THREADS = 256;
 constexpr int BW_T = 32;                  // keys per dq tile / queries per dk, dv chunk
 constexpr float kInf = __builtin_inff();
 
-// One staged 32 x D tile: row-major with XOR-swizzled 16-byte chunks, and
-// transposed ([D][32 + 8]) with the accumulator order of the 32 rows.
+// One staged 32 x D tile, row-major, loaded straight into LDS.  It is read
+// two ways: by rows (16-byte chunks, one row per lane) and by the LDS
+// transpose load (ds_read_b64_tr_b16: within each 16-lane group lane i gets
+// element i mod 4 of the 8 bytes lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4
+// addressed, a 4-row x 16-column transpose; two of them give an MFMA lane 8
+// consecutive rows of one column).  The chunk swizzle serves both: XOR by
+// 0, 6, 12, 10 (d = 128; 0, 6, 4, 2 for d = 64) for rows = 0..3 mod 4, which
+// spreads a transpose load's four rows over distinct banks, then by
+// (row / 4) mod 4, which makes it a permutation over 16 consecutive rows for
+// the row reads.
 template <int D>
 struct BwTile {
     static constexpr int CPR = D / 8;
-    static constexpr int TSTR = BW_T + 8;            // bf16 per transposed row (16-B pad)
-    static constexpr int ROW = BW_T * D;             // row-major elements
-    static constexpr int TRN = D * TSTR;             // transposed elements
-    static constexpr int NST = BW_T * D / 16;        // threads staging it (2 rows x 8 dims each)
+    static constexpr int ROW = BW_T * D;             // elements
+    static constexpr int INST = ROW / 8 / BW_THREADS;   // 16-byte load-to-LDS per thread
 };
+
+template <int CPR>
+__device__ __forceinline__ int bswz(int r) {
+    const int a = CPR == 16 ? ((0xAC60 >> (4 * (r & 3))) & 15) : ((0x2460 >> (4 * (r & 3))) & 7);
+    return (a ^ ((r >> 2) & 3)) & (CPR - 1);
+}
 
 // Row-major 16-byte chunk (row r, logical chunk cc) position in elements.
 template <int D>
 __device__ __forceinline__ int bw_rm(int r, int cc) {
-    return r * D + ((cc ^ kswz<D / 8>(r)) * 8);
+    return r * D + ((cc ^ bswz<D / 8>(r)) * 8);
 }
 
-// Thread t < NST holds rows 2*(t % 16) + {0, 1}, dims 8*(t / 16) .. +7 of a
-// tile: write them row-major and transposed.
+// Element offset, inside a tile, of this lane's transpose load for columns
+// 32*db + (lane % 32) and rows 16*c16 + 8*rd + 4*(lane / 32) + 0..3.
 template <int D>
-__device__ __forceinline__ void bw_store_both(uint16_t* rm, uint16_t* tr, const u32x4* x, int t) {
-    using L = BwTile<D>;
-    const int kq = t % 16, vdc = t / 16;
-    const int r0 = 2 * kq;
-    *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0, vdc)) = x[0];
-    *reinterpret_cast<u32x4*>(rm + bw_rm<D>(r0 + 1, vdc)) = x[1];
-    const int pos = swap23(r0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        *reinterpret_cast<uint32_t*>(tr + (vdc * 8 + j) * L::TSTR + pos) =
-            __builtin_amdgcn_perm(x[1][w], x[0][w], sel);
-    }
+__device__ __forceinline__ int bw_tr_offset(int lane, int db, int c16, int rd) {
+    const int gi = lane >> 4, a = lane & 15;
+    const int row = 16 * c16 + 8 * rd + 4 * (gi >> 1) + (a >> 2);
+    const int chunk = db * 4 + 2 * (gi & 1) + ((a & 3) >> 1);
+    return row * D + ((chunk ^ bswz<D / 8>(row)) * 8) + 4 * (a & 1);
 }
 
-// The same rows, transposed only.
+typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+
+// A operand (rows = columns 32*db.. of the tile, k = tile rows 16*c16 ..
+// +15 in the accumulator order) by two transpose loads.
 template <int D>
-__device__ __forceinline__ void bw_store_tr(uint16_t* tr, const u32x4* x, int t) {
-    using L = BwTile<D>;
-    const int kq = t % 16, vdc = t / 16;
-    const int pos = swap23(2 * kq);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        *reinterpret_cast<uint32_t*>(tr + (vdc * 8 + j) * L::TSTR + pos) =
-            __builtin_amdgcn_perm(x[1][w], x[0][w], sel);
-    }
+__device__ __forceinline__ bf16x8 bw_tr_operand(const uint16_t* tile, int lane, int db, int c16) {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(tile + bw_tr_offset<D>(lane, db, c16, 0)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(tile + bw_tr_offset<D>(lane, db, c16, 1)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Load-to-LDS offsets: chunk p = (i * 4 + wave) * 64 + lane of the tile holds
+// row p / CPR, logical chunk (p % CPR) ^ swizzle.
+template <int D>
+__device__ __forceinline__ uint32_t bw_src_offset(int i, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    const int p = (i * PF_WAVES + wave) * 64 + lane;
+    const int r = p / CPR;
+    return (uint32_t)(r * D + ((p % CPR) ^ bswz<CPR>(r)) * 8) * 2;
 }
 
 // ------------------------------------------------------------------ prep --
@@ -124,7 +133,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               uint16_t* __restrict__ dq, int Hq, int Hkv, int N, int BH, int n_qtiles, float c,
               float scale) {
     using L = BwTile<D>;
-    constexpr int STAGE = 2 * L::ROW + L::TRN;       // K, V row-major + K^T
+    constexpr int STAGE = 2 * L::ROW;                // K, V row-major
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -162,35 +171,18 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int row_end = min(q0 + PF_BM, N);
     const int n_kt = CAUSAL ? (row_end + BW_T - 1) / BW_T : (N + BW_T - 1) / BW_T;
 
-    // Staging: thread t < NST loads K rows 2*(t%16) + {0,1}, dims 8*(t/16)..+7
-    // into registers (written row-major and transposed); V goes straight to
-    // LDS, chunk p = i * 256 + tid of the tile.
-    constexpr int VINST = L::ROW / 8 / BW_THREADS;   // 2 (D = 128) or 1 (D = 64)
-    const bool kst = tid < L::NST;
-    const uint32_t koff = (uint32_t)((2 * (tid % 16)) * D + (tid / 16) * 8) * 2;
-    uint32_t voff[VINST];
+    uint32_t soff[L::INST];
 #pragma unroll
-    for (int i = 0; i < VINST; ++i) {
-        const int p = (i * PF_WAVES + wave) * 64 + lane;
-        const int r = p / L::CPR;
-        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
-        voff[i] = (uint32_t)(r * D + cc * 8) * 2;
-    }
-    u32x4 kreg[2];
+    for (int i = 0; i < L::INST; ++i) soff[i] = bw_src_offset<D>(i, wave, lane);
 
     auto issue_loads = [&](int kt, int buf) {
         const uint32_t t0 = (uint32_t)kt * BW_T * D * 2;
-        uint16_t* Vs = smem + buf * STAGE + L::ROW;
+        uint16_t* Ks = smem + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < VINST; ++i)
-            buf_ld16_lds(vrs, Vs + (i * PF_WAVES + wave) * 64 * 8, t0 + voff[i]);
-        if (kst) {
-            kreg[0] = buf_ld16(krs, t0 + koff);
-            kreg[1] = buf_ld16(krs, t0 + koff + D * 2);
+        for (int i = 0; i < L::INST; ++i) {
+            buf_ld16_lds(krs, Ks + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
+            buf_ld16_lds(vrs, Ks + L::ROW + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
         }
-    };
-    auto store_k = [&](int buf) {
-        if (kst) bw_store_both<D>(smem + buf * STAGE, smem + buf * STAGE + 2 * L::ROW, kreg, tid);
     };
 
     f32x16 acc[D / 32];
@@ -201,7 +193,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    store_k(0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -212,7 +203,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         if (wave_active && (!CAUSAL || k0 <= wrow0 + 31)) {
             const uint16_t* Ks = smem + buf * STAGE;
             const uint16_t* Vs = Ks + L::ROW;
-            const uint16_t* Kt = Ks + 2 * L::ROW;
             // S^T = K Q^T and dP^T = V dO^T for the tile's 32 keys.
             f32x16 sacc, pacc;
 #pragma unroll
@@ -238,7 +228,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 }
                 sacc[r] = p * (pacc[r] - drow);
             }
-            // dQ^T += K^T dS^T, 16 keys per MFMA.
+            // dQ^T += K^T dS^T, 16 keys per MFMA; K^T by transpose loads.
 #pragma unroll
             for (int c16 = 0; c16 < BW_T / 16; ++c16) {
                 bf16x8 sb;
@@ -246,16 +236,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 for (int i = 0; i < 8; ++i) sb[i] = (__bf16)sacc[c16 * 8 + i];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        Kt + (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8);
+                    const bf16x8 a = bw_tr_operand<D>(Ks, lane, db, c16);
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[db], 0, 0, 0);
                 }
             }
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);
-            store_k(buf ^ 1);
-        }
+        if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
     }
 
@@ -280,19 +266,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // are staged in LDS.  Splitting dV from dK recomputes S once more but keeps
 // each pass within two waves per SIMD (a fused pass would hold both 32-key
 // accumulator tiles, K and V, and spill).
-//   dV pass: S = Q K^T, P = 2^(c s - lse2), dV^T += dO^T P  (Q row-major, dO^T)
-//   dK pass: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS (Q both ways, dO)
+//   dV pass: S = Q K^T, P = 2^(c s - lse2), dV^T += dO^T P
+//   dK pass: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+// Q and dO are staged row-major; dO^T and Q^T come from transpose loads.
 constexpr int kDV = 0, kDK = 1;
 constexpr int kKvRun = 4;           // key tiles of one head kept on one XCD
 
-template <int D, int MODE>
+template <int D>
 struct KvStage {
     using L = BwTile<D>;
     // element offsets inside one stage
     static constexpr int QRM = 0;                                   // Q row-major
-    static constexpr int SEC = L::ROW;                              // dO^T (dV) or dO row-major (dK)
-    static constexpr int QTR = SEC + (MODE == kDV ? L::TRN : L::ROW);   // Q^T (dK only)
-    static constexpr int STATS = QTR + (MODE == kDV ? 0 : L::TRN);  // lse2 [32], D [32] as floats
+    static constexpr int GRM = L::ROW;                              // dO row-major
+    static constexpr int STATS = 2 * L::ROW;                        // lse [32], D [32] as floats
     static constexpr int SIZE = STATS + 2 * BW_T * 2;
 };
 
@@ -304,7 +290,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               uint16_t* __restrict__ out, float* __restrict__ out32, int Hq, int Hkv, int N, int BH,
               float c, float scale) {
     using L = BwTile<D>;
-    using St = KvStage<D, MODE>;
+    using St = KvStage<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * St::SIZE];
 
     const int tid = threadIdx.x;
@@ -348,38 +334,22 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int c_first = CAUSAL ? key0 / BW_T : 0;
     const int n_c = (N + BW_T - 1) / BW_T;
 
-    // Staging.  The tensor needed both ways (dV: dO, only transposed; dK: Q)
-    // goes through registers: thread t < NST holds rows 2*(t%16) + {0,1},
-    // dims 8*(t/16) .. +7.  The one needed row-major only (dV: Q, dK: dO)
-    // goes straight to LDS, chunk p = i * 256 + tid of the tile.
-    constexpr int RINST = L::ROW / 8 / BW_THREADS;
-    const bool st = tid < L::NST;
-    const uint32_t soff = (uint32_t)((2 * (tid % 16)) * D + (tid / 16) * 8) * 2;
-    uint32_t roff[RINST];
+    // Staging: Q and dO chunks straight to LDS; lse (base 2) and D through
+    // registers (32 values each).
+    uint32_t soff[L::INST];
 #pragma unroll
-    for (int i = 0; i < RINST; ++i) {
-        const int p = (i * PF_WAVES + wave) * 64 + lane;
-        const int r = p / L::CPR;
-        const int cc = (p % L::CPR) ^ kswz<L::CPR>(r);
-        roff[i] = (uint32_t)(r * D + cc * 8) * 2;
-    }
-    const __amdgpu_buffer_rsrc_t reg_rs = MODE == kDV ? ors : qrs;   // through registers
-    const __amdgpu_buffer_rsrc_t lds_rs = MODE == kDV ? qrs : ors;   // straight to LDS
-    constexpr int LDS_DST = MODE == kDV ? St::QRM : St::SEC;
-    u32x4 sreg[2];
+    for (int i = 0; i < L::INST; ++i) soff[i] = bw_src_offset<D>(i, wave, lane);
     float lreg = 0.f, dreg = 0.f;
     const float* lse_h = lse + (size_t)bh * N;
     const float* del_h = delta + (size_t)bh * N;
 
     auto issue_loads = [&](int cj, int buf) {
         const uint32_t t0 = (uint32_t)cj * BW_T * D * 2;
-        uint16_t* dst = smem + buf * St::SIZE + LDS_DST;
+        uint16_t* base = smem + buf * St::SIZE;
 #pragma unroll
-        for (int i = 0; i < RINST; ++i)
-            buf_ld16_lds(lds_rs, dst + (i * PF_WAVES + wave) * 64 * 8, t0 + roff[i]);
-        if (st) {
-            sreg[0] = buf_ld16(reg_rs, t0 + soff);
-            sreg[1] = buf_ld16(reg_rs, t0 + soff + D * 2);
+        for (int i = 0; i < L::INST; ++i) {
+            buf_ld16_lds(qrs, base + St::QRM + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
+            buf_ld16_lds(ors, base + St::GRM + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
         }
         if (tid < BW_T) {
             const int qi = cj * BW_T + tid;
@@ -388,16 +358,8 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
     };
     auto store = [&](int buf) {
-        uint16_t* base = smem + buf * St::SIZE;
-        if (st) {
-            if constexpr (MODE == kDV) {
-                bw_store_tr<D>(base + St::SEC, sreg, tid);
-            } else {
-                bw_store_both<D>(base + St::QRM, base + St::QTR, sreg, tid);
-            }
-        }
         if (tid < BW_T) {
-            float* stats = reinterpret_cast<float*>(base + St::STATS);
+            float* stats = reinterpret_cast<float*>(smem + buf * St::SIZE + St::STATS);
             stats[tid] = lreg;
             stats[BW_T + tid] = dreg;
         }
@@ -434,7 +396,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(base + St::QRM + e);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
                 if constexpr (MODE == kDK) {
-                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(base + St::SEC + e);
+                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(base + St::GRM + e);
                     pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
                 }
             }
@@ -458,8 +420,9 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     sacc[r] = p;
                 }
             }
-            // dV^T += dO^T P, or dK^T += Q^T dS: 16 queries per MFMA.
-            const uint16_t* At = base + (MODE == kDV ? St::SEC : St::QTR);
+            // dV^T += dO^T P, or dK^T += Q^T dS: 16 queries per MFMA, the
+            // transposed operand by transpose loads from the row-major tile.
+            const uint16_t* At = base + (MODE == kDV ? St::GRM : St::QRM);
 #pragma unroll
             for (int c16 = 0; c16 < BW_T / 16; ++c16) {
                 bf16x8 pb;
@@ -467,8 +430,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[c16 * 8 + i];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        At + (db * 32 + l32) * L::TSTR + c16 * 16 + hi * 8);
+                    const bf16x8 a = bw_tr_operand<D>(At, lane, db, c16);
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
                 }
             }
