@@ -133,8 +133,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               uint16_t* __restrict__ dq, int Hq, int Hkv, int N, int BH, int n_qtiles, float c,
               float scale) {
     using L = BwTile<D>;
-    constexpr int STAGE = 2 * L::ROW;                // K, V row-major
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    // K and V row-major; two buffers as separate LDS arrays (the loop is
+    // unrolled by two so the compiler sees the loads into one do not alias
+    // the reads of the other)
+    __shared__ __attribute__((aligned(16))) uint16_t smem0[2 * L::ROW];
+    __shared__ __attribute__((aligned(16))) uint16_t smem1[2 * L::ROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -175,9 +178,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < L::INST; ++i) soff[i] = bw_src_offset<D>(i, wave, lane);
 
-    auto issue_loads = [&](int kt, int buf) {
+    auto issue_loads = [&](int kt, uint16_t* Ks) {
         const uint32_t t0 = (uint32_t)kt * BW_T * D * 2;
-        uint16_t* Ks = smem + buf * STAGE;
 #pragma unroll
         for (int i = 0; i < L::INST; ++i) {
             buf_ld16_lds(krs, Ks + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
@@ -191,17 +193,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    issue_loads(0, 0);
+    issue_loads(0, smem0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
+    auto step = [&](int kt, const uint16_t* Ks, uint16_t* nxt) {
         const bool more = kt + 1 < n_kt;
-        if (more) issue_loads(kt + 1, buf ^ 1);
+        if (more) issue_loads(kt + 1, nxt);
         const int k0 = kt * BW_T;
         if (wave_active && (!CAUSAL || k0 <= wrow0 + 31)) {
-            const uint16_t* Ks = smem + buf * STAGE;
             const uint16_t* Vs = Ks + L::ROW;
             // S^T = K Q^T and dP^T = V dO^T for the tile's 32 keys.
             f32x16 sacc, pacc;
@@ -243,6 +243,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < n_kt) step(kt + 1, smem1, smem0);
     }
 
     if (row_ok) {
@@ -278,9 +282,10 @@ struct KvStage {
     // element offsets inside one stage
     static constexpr int QRM = 0;                                   // Q row-major
     static constexpr int GRM = L::ROW;                              // dO row-major
-    static constexpr int STATS = 2 * L::ROW;                        // lse [32], D [32] as floats
-    static constexpr int SIZE = STATS + 2 * BW_T * 2;
+    static constexpr int STATS = 2 * L::ROW;                        // lse [64], D [64] as floats
+    static constexpr int SIZE = STATS + 2 * 64 * 2;
 };
+constexpr int kKvStages = 3;        // query chunks in LDS: one computing, two loading
 
 template <int D, bool CAUSAL, int MODE>
 __global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -291,7 +296,11 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               float c, float scale) {
     using L = BwTile<D>;
     using St = KvStage<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * St::SIZE];
+    // the ring of chunks: separate LDS arrays, the loop unrolled by three (see
+    // the dq kernel)
+    __shared__ __attribute__((aligned(16))) uint16_t ring0[St::SIZE];
+    __shared__ __attribute__((aligned(16))) uint16_t ring1[St::SIZE];
+    __shared__ __attribute__((aligned(16))) uint16_t ring2[St::SIZE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -334,35 +343,27 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int c_first = CAUSAL ? key0 / BW_T : 0;
     const int n_c = (N + BW_T - 1) / BW_T;
 
-    // Staging: Q and dO chunks straight to LDS; lse (base 2) and D through
-    // registers (32 values each).
+    // Staging: Q and dO chunks, lse and D (64 values from the chunk's first
+    // query; rows past N read as zero and are masked) all straight to LDS, in
+    // a ring of kKvStages chunks.  Every wave issues the same loads (the
+    // stats redundantly), so one vmcnt threshold fits all.
     uint32_t soff[L::INST];
 #pragma unroll
     for (int i = 0; i < L::INST; ++i) soff[i] = bw_src_offset<D>(i, wave, lane);
-    float lreg = 0.f, dreg = 0.f;
-    const float* lse_h = lse + (size_t)bh * N;
-    const float* del_h = delta + (size_t)bh * N;
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+    constexpr int OPS = 2 * L::INST + 1 + (MODE == kDK ? 1 : 0);   // vector memory ops per chunk
 
-    auto issue_loads = [&](int cj, int buf) {
+    auto issue_loads = [&](int cj, uint16_t* base) {
         const uint32_t t0 = (uint32_t)cj * BW_T * D * 2;
-        uint16_t* base = smem + buf * St::SIZE;
 #pragma unroll
         for (int i = 0; i < L::INST; ++i) {
             buf_ld16_lds(qrs, base + St::QRM + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
             buf_ld16_lds(ors, base + St::GRM + (i * PF_WAVES + wave) * 64 * 8, t0 + soff[i]);
         }
-        if (tid < BW_T) {
-            const int qi = cj * BW_T + tid;
-            lreg = qi < N ? lse_h[qi] * kLog2e : kInf;
-            if constexpr (MODE == kDK) dreg = qi < N ? del_h[qi] : 0.f;
-        }
-    };
-    auto store = [&](int buf) {
-        if (tid < BW_T) {
-            float* stats = reinterpret_cast<float*>(smem + buf * St::SIZE + St::STATS);
-            stats[tid] = lreg;
-            stats[BW_T + tid] = dreg;
-        }
+        const uint32_t so = (uint32_t)(cj * BW_T + lane) * 4;
+        buf_ld4_lds(lrs, base + St::STATS, so);
+        if constexpr (MODE == kDK) buf_ld4_lds(drs, base + St::STATS + 128, so);
     };
 
     f32x16 acc[D / 32];
@@ -371,19 +372,24 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    issue_loads(c_first, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    store(0);
-    __syncthreads();
+    const int nq = n_c - c_first;                    // >= 1 (key0 < N)
+    issue_loads(c_first, ring0);
+    if (nq > 1) issue_loads(c_first + 1, ring1);
 
-    for (int cj = c_first; cj < n_c; ++cj) {
-        const int buf = (cj - c_first) & 1;
-        const bool more = cj + 1 < n_c;
-        if (more) issue_loads(cj + 1, buf ^ 1);
+    // chunk t of the ring: wait for its loads (those of chunk t+1 may stay in
+    // flight), barrier, start chunk t+2 into the buffer chunk t-1 used, compute
+    auto step = [&](int t, const uint16_t* base, uint16_t* nxt2) {
+        const int cj = c_first + t;
+        if (t + 1 < nq) wait_vmcnt<OPS>(); else wait_vmcnt<0>();
+        // a plain barrier (no fence, which would drain every load in flight);
+        // the memory clobber keeps the compiler from moving LDS accesses
+        // across it, and every LDS read of the previous chunk has been
+        // consumed by its MFMAs before a wave gets here
+        asm volatile("s_barrier" ::: "memory");
+        if (t + 2 < nq) issue_loads(cj + 2, nxt2);
         const int qc = cj * BW_T;
         // skip a chunk whose queries all precede this wave's keys
         if (wave_active && (!CAUSAL || qc + BW_T - 1 >= wkey0)) {
-            const uint16_t* base = smem + buf * St::SIZE;
             const float* stats = reinterpret_cast<const float*>(base + St::STATS);
             // S = Q K^T (and dP = dO V^T): lane = key, entry r = query
             // qc + 8(r/4) + 4hi + r%4.
@@ -406,11 +412,11 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             for (int rg = 0; rg < 4; ++rg) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
                 f32x4 d4;
-                if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + BW_T + 8 * rg + 4 * hi);
+                if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + 64 + 8 * rg + 4 * hi);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rg * 4 + i;
-                    float p = fast_exp2(fmaf(sacc[r], c, -l4[i]));
+                    float p = fast_exp2(fmaf(sacc[r], c, -l4[i] * kLog2e));
                     if (need_mask) {
                         const int qi = qc + 8 * rg + 4 * hi + i;
                         const bool ok = qi < N && mykey < N && (!CAUSAL || mykey <= qi);
@@ -435,11 +441,11 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 }
             }
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);
-            store(buf ^ 1);
-        }
-        __syncthreads();
+    };
+    for (int t = 0; t < nq; t += 3) {
+        step(t, ring0, ring2);
+        if (t + 1 < nq) step(t + 1, ring1, ring0);
+        if (t + 2 < nq) step(t + 2, ring2, ring1);
     }
 
     if (mykey < N) {

@@ -62,6 +62,21 @@ __device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
 }
 
+// 4 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds_base + 4*l.
+__device__ __forceinline__ void buf_ld4_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, off, 0, 0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding (loads complete in issue order); LDS and export counters are
+// not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Wave-wide exchange with lane ^ mask (ds_bpermute based).
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
     return __shfl_xor(x, mask, 64);

@@ -21,8 +21,9 @@
 //     (converted to bf16); V^T comes from the row-major V tile through LDS
 //     transpose loads (two per MFMA), which deliver 8 keys of one dim per
 //     lane in the key order of the accumulator lanes.
-//   * K/V tiles are double-buffered in LDS; the loads of tile j+1 are issued
-//     before the MFMA work on tile j.  K and V go straight from memory into
+//   * K/V tiles are double-buffered in LDS (two separate arrays, the loop
+//     unrolled by two); the loads of tile j+1 are issued before the MFMA work
+//     on tile j.  K and V go straight from memory into
 //     LDS (buffer_load ... lds), their 16-byte chunks XOR-swizzled per row so
 //     the operand fetches of each are free of bank conflicts.  Buffer
 //     resources bound every load by the head's extent, so rows past N read
@@ -46,7 +47,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
                     float c, int negate) {
     using L = PfLayout<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t smem0[L::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t smem1[L::BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -101,9 +103,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         voff[i] = (uint32_t)(r * D + cc * 8) * 2;
     }
 
-    auto issue_loads = [&](int kt, int buf) {
+    auto issue_loads = [&](int kt, uint16_t* Ks) {
         const uint32_t t0 = (uint32_t)kt * PF_BN * D * 2;
-        uint16_t* Ks = smem + buf * L::BUF;
         uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
         for (int i = 0; i < L::KINST; ++i)
@@ -120,24 +121,31 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    issue_loads(0, 0);
+    issue_loads(0, smem0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
+    // One key tile: compute from `cur` while the next one loads into `nxt`.
+    // The two buffers are separate LDS arrays and the loop is unrolled by two,
+    // so every access names its buffer: the compiler can then tell that the
+    // transpose loads of `cur` do not read what the loads into `nxt` write,
+    // and does not drain those loads before them.
+    auto step = [&](int kt, const uint16_t* cur, uint16_t* nxt) {
         const bool more = kt + 1 < n_kt;
-        if (more) issue_loads(kt + 1, buf ^ 1);
+        if (more) issue_loads(kt + 1, nxt);
         const int k0 = kt * PF_BN;
         const bool compute = wave_active && (!CAUSAL || k0 <= wrow0 + 31);
         if (compute) {
-            const uint16_t* Ks = smem + buf * L::BUF;
             const bool need_mask = (k0 + PF_BN > N) || (CAUSAL && k0 + PF_BN - 1 > wrow0);
-            pf_tile_step<D, CAUSAL>(Ks, Ks + L::KELEMS, qf, oacc, m_run, l_run, k0, N, myrow,
+            pf_tile_step<D, CAUSAL>(cur, cur + L::KELEMS, qf, oacc, m_run, l_run, k0, N, myrow,
                                     need_mask, c, hi, l32);
         }
         if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < n_kt) step(kt + 1, smem1, smem0);
     }
 
     // Epilogue: o = u / l, lse = m + ln l (natural log).

@@ -55,7 +55,8 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     using L = PfLayout<D>;
     constexpr int BS = kDecodeBlock;
     static_assert(PF_BN == PF_WAVES * BS, "one cache block per wave per key tile");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t smem0[L::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t smem1[L::BUF];
     __shared__ int bad_s[PF_WAVES];
     __shared__ int rank_cost[kRankPairs];
     __shared__ int rank_pick;
@@ -159,7 +160,7 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int32_t* trow = table + (size_t)s * max_blocks;
     int bad = 0x7fffffff;                                     // lowest block with a bad entry
 
-    auto issue_loads = [&](int kt, int buf) {
+    auto issue_loads = [&](int kt, uint16_t* Ks) {
         const int blk = kt * PF_WAVES + wave;
         const int valid = min(max(ctx - blk * BS, 0), BS);    // rows of this block in the sequence
         int phys = 0;
@@ -177,7 +178,6 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const uint32_t bytes = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)valid * D * 2 : 0u);
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + base, bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + base, bytes);
-        uint16_t* Ks = smem + buf * L::BUF;
         uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
         for (int i = 0; i < L::KINST; ++i)
@@ -196,23 +196,27 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int mypos = first + myrow;
     const int wpos0 = first + wrow0;
 
-    issue_loads(0, 0);
+    issue_loads(0, smem0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
+    // One key tile from `cur` while the next loads into `nxt` (separate LDS
+    // arrays, loop unrolled by two, so the compiler sees they do not alias).
+    auto step = [&](int kt, const uint16_t* cur, uint16_t* nxt) {
         const bool more = kt + 1 < n_kt;
-        if (more) issue_loads(kt + 1, buf ^ 1);
+        if (more) issue_loads(kt + 1, nxt);
         const int k0 = kt * PF_BN;
         if (wave_active && k0 <= wpos0 + 31) {
-            const uint16_t* Ks = smem + buf * L::BUF;
             const bool need_mask = k0 + PF_BN - 1 > wpos0;
-            pf_tile_step<D, true>(Ks, Ks + L::KELEMS, qf, oacc, m_run, l_run, k0, ctx, mypos,
+            pf_tile_step<D, true>(cur, cur + L::KELEMS, qf, oacc, m_run, l_run, k0, ctx, mypos,
                                   need_mask, c, hi, l32);
         }
         if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
         __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < n_kt) step(kt + 1, smem1, smem0);
     }
 
     // Lowest bad block seen by any wave of the workgroup.
