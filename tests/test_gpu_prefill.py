@@ -330,3 +330,23 @@ def test_config_long_causal_sampled(name):
     rng = np.random.default_rng(123)
     check_dense_rows(o, lse, f64(q), f64(k), f64(v), cfg.scale, True,
                      _row_samples(rng, cfg.B, cfg.Hq, cfg.N, 24), cfg.name)
+
+
+def test_long_prefill_allocates_nothing():
+    """T = 32768, 16 heads: with o and lse passed in, the call leaves torch's
+    peak allocation and the device's free memory where they were (the fp32
+    score matrix the tiles avoid would be 16 * 32768^2 * 4 B = 68.7 GB)."""
+    from exact_tiled_self_amd import attn_fwd
+    cfg = DENSE_CONFIGS["mha_causal_t32768"]
+    q, k, v = (t.to(DEV) for t in dense_inputs(cfg))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    peak0 = torch.cuda.max_memory_allocated()
+    free0 = torch.cuda.mem_get_info()[0]
+    attn_fwd(q, k, v, scale=cfg.scale, causal=True, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == peak0
+    assert abs(torch.cuda.mem_get_info()[0] - free0) < (64 << 20)
+    assert torch.isfinite(o[0, :, -1].float()).all()
