@@ -106,7 +106,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     // per-head byte offsets (plus one tile of look-ahead) must fit 32 bits
     if ((long long)N * d > (1LL << 31) - (1LL << 16))
         return fail(ATTN_ERR_UNSUPPORTED, "N * d must be at most 2^31 - 2^16");
-    const long long grid = (long long)B * Hq * ((N + 63) / 64);
+    const int rows_per_wg = dtype == ATTN_F32 ? 16 : 64;   // the smallest row tile of either kernel
+    const long long grid = (long long)B * Hq * ((N + rows_per_wg - 1) / rows_per_wg);
     if (grid >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
