@@ -16,13 +16,13 @@
 //     and dP^T = V dO^T on MFMA (a lane owns one query row, so lse_i and D_i
 //     are per-lane scalars), dS^T in registers, then dQ^T += K^T dS^T with
 //     dS^T taken straight from the accumulators as the B operand.  K and V
-//     are staged row-major (XOR-swizzled 16-byte chunks) and K^T transposed
-//     with the accumulator key order (bits 2 and 3 of the key swapped).
+//     tiles go straight to LDS, row-major; K^T is read from the K tile with
+//     LDS transpose loads.  Two buffers, one loading while one computes.
 //   * bwd_kv (twice): 4 waves x 32 keys, query chunks of 32; a lane owns one
 //     key, its K (and V) rows stay in registers.  The dV pass computes
 //     S = Q K^T, P and dV^T += dO^T P; the dK pass S, dP = dO V^T,
-//     dS = P (dP - D) and dK^T += Q^T dS.  lse and D per query go through
-//     LDS.
+//     dS = P (dP - D) and dK^T += Q^T dS.  Q, dO, lse and D go straight to
+//     LDS in a ring of three chunks; dO^T and Q^T come from transpose loads.
 //   * bwd_reduce: with grouped K/V heads the two passes write one fp32
 //     dk, dv per query head into the workspace and this kernel sums each
 //     group in head order into the bf16 outputs.
@@ -285,7 +285,6 @@ struct KvStage {
     static constexpr int STATS = 2 * L::ROW;                        // lse [64], D [64] as floats
     static constexpr int SIZE = STATS + 2 * 64 * 2;
 };
-constexpr int kKvStages = 3;        // query chunks in LDS: one computing, two loading
 
 template <int D, bool CAUSAL, int MODE>
 __global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -345,7 +344,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     // Staging: Q and dO chunks, lse and D (64 values from the chunk's first
     // query; rows past N read as zero and are masked) all straight to LDS, in
-    // a ring of kKvStages chunks.  Every wave issues the same loads (the
+    // a ring of three chunks (one computing, two loading).  Every wave issues the same loads (the
     // stats redundantly), so one vmcnt threshold fits all.
     uint32_t soff[L::INST];
 #pragma unroll

@@ -57,12 +57,6 @@ __device__ __forceinline__ int vswz(int r) {
     return (0xAC60 >> (4 * (r & 3))) & 15 & (CPR - 1);
 }
 
-// Position of key x (within a 16-key group) in a transposed tile stored with
-// the accumulator key order: bits 2 and 3 exchanged.  It is its own inverse.
-__device__ __forceinline__ int swap23(int x) {
-    return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Per-lane element offsets (inside a V tile, before the key-block term) of
