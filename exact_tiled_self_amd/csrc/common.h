@@ -82,6 +82,17 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
     return __shfl_xor(x, mask, 64);
 }
 
+// max(x of this lane, x of lane l ^ 32) with v_permlane32_swap, a VALU
+// exchange between the two 32-lane halves of the wave (no LDS traffic).  With
+// the same register as both operands, one result holds the lower half's
+// values in both halves' positions swapped in and the other the upper half's,
+// so their maximum is the pairwise maximum in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);

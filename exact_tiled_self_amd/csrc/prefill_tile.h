@@ -88,6 +88,44 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
                                              int kend, int mypos, bool need_mask, float c, int hi,
                                              int l32) {
     using L = PfLayout<D>;
+    constexpr int KS = D / 16;           // k-steps of the score product
+    constexpr int KPF = KS < 4 ? KS : 4; // K operand pairs read ahead of their MFMAs
+    const int lane = hi * 32 + l32;
+
+    // Operand reads are issued ahead of the MFMAs that consume them (the
+    // scheduling barriers keep the compiler from sinking them back to their
+    // uses), so an LDS round trip overlaps the matrix work instead of
+    // preceding every MFMA.
+    bf16x8 ka[KS][PF_BN / 32];
+    auto kread = [&](int ks) {
+#pragma unroll
+        for (int kb = 0; kb < PF_BN / 32; ++kb) {
+            const int r = kb * 32 + l32;
+            const int cc = (ks * 2 + hi) ^ kswz<L::CPR>(r);
+            ka[ks][kb] = *reinterpret_cast<const bf16x8*>(Ks + (r * D + cc * 8));
+        }
+    };
+    // V^T operand of key block c16 (16 keys), dims block db: two transpose
+    // loads.  Each per-lane base is one opaque element offset from Vs, so
+    // every read's address stays a short chain from the LDS array: the
+    // compiler can then see that these reads do not touch the other buffer,
+    // which the next tile's loads are filling, and does not wait for them.
+    const uint16_t* vbase[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        int off = pf_vtr_offset<D>(lane, db);
+        asm("" : "+v"(off));
+        vbase[db] = Vs + off;
+    }
+    auto vread = [&](int c16, bf16x8* dst) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[db] + c16 * 16 * D));
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[db] + c16 * 16 * D + 8 * D));
+            dst[db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
     // S^T = K Q^T for the 64 keys of this tile (two 32-key blocks).
     f32x16 sacc[PF_BN / 32];
 #pragma unroll
@@ -95,15 +133,21 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KPF; ++ks) kread(ks);
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb) {
-            const int r = kb * 32 + l32;
-            const int cc = (ks * 2 + hi) ^ kswz<L::CPR>(r);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (r * D + cc * 8));
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + KPF < KS) kread(ks + KPF);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < PF_BN / 32; ++kb)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
+
+    // The first V^T operands are read now; the softmax below hides them.
+    bf16x8 va[2][D / 32];
+    vread(0, va[0]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Lane key of accumulator entry r in block kb: k0 + 32kb + 8(r/4) + 4hi + r%4.
     float mx = kNegInf;
@@ -123,7 +167,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     }
-    mx = fmaxf(mx, xor_shfl(mx, 32));
+    mx = max_halves(mx);
 
     // Lazy rescale: a wave-uniform branch taken only when some row's
     // maximum grew by more than 2^kLazyLog2 (always on the first tile).
@@ -161,23 +205,22 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
             }
     }
     l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T P^T, 16 keys per MFMA; V^T by two transpose loads.
-    const int lane = hi * 32 + l32;
+    // O^T += V^T P^T, 16 keys per MFMA; the operands of the next key block
+    // are read while the current one's MFMAs run.
 #pragma unroll
     for (int c16 = 0; c16 < PF_BN / 16; ++c16) {
+        if (c16 + 1 < PF_BN / 16) vread(c16 + 1, va[(c16 + 1) & 1]);
         const int kb = c16 >> 1, sh = (c16 & 1) * 8;
         bf16x8 pb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[kb][sh + i];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* v0 = Vs + pf_vtr_offset<D>(lane, db) + c16 * 16 * D;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v0));
-            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v0 + 8 * D));
-            const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-        }
+        for (int db = 0; db < D / 32; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c16 & 1][db], pb, oacc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
