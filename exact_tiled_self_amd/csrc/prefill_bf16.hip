@@ -33,6 +33,12 @@
 //   * Causal: tiles entirely above the diagonal are never visited, the q
 //     tiles are dispatched heaviest first, and a wave whose rows all lie
 //     before a tile skips its arithmetic for it.
+//
+// Two kernels share this layout: prefill_bf16_kernel runs each key tile's
+// phases in order (tile step in prefill_tile.h); prefill_sp_kernel, used for
+// causal d = 128, software-pipelines them inside each wave (see its comment).
+
+#include <type_traits>
 
 #include "internal.h"
 #include "prefill_tile.h"
@@ -167,15 +173,333 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
+// Software-pipelined variant: inside each wave, the vector work of key
+// tile j runs between the matrix instructions of its neighbours, because a
+// wave's own independent VALU instructions issue while its MFMAs execute
+// (the matrix core and the vector unit then work at once), which two
+// separate waves on a SIMD do not achieve.  Per tile j, after the rescale
+// check of tile j:
+//   block A: S^T(j+1) = K(j+1) Q^T (16 MFMAs)  beside  P(j) = 2^(c s - c m),
+//            its row sum and bf16 packing
+//   block B: O^T += V^T(j) P^T(j) (16 MFMAs)    beside  the row maximum of
+//            tile j+1 (masked where needed)
+// K and V have separate double buffers: block A reads K(j+1) and block B
+// V(j), so both stay resident for one iteration while K(j+2) and V(j+1)
+// load into the other halves.  The arithmetic per row is the same as in
+// prefill_bf16_kernel (same products, same order), only interleaved.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                  const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                  float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
+                  float c, int negate) {
+    constexpr int CPR = D / 8;
+    constexpr int TILE = PF_BN * D;
+    constexpr int LINST = PF_BN * CPR / PF_THREADS;
+    constexpr int KS = D / 16;
+    constexpr int NDB = D / 32;
+    static_assert(LINST * PF_THREADS == PF_BN * CPR, "tile split");
+    __shared__ __attribute__((aligned(16))) uint16_t kbuf0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t kbuf1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf1[TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hi = lane >> 5, l32 = lane & 31;
+
+    // Work unit: (b, h, q tile); heaviest q tiles first when causal.
+    const int wg = blockIdx.x;
+    const int qt = CAUSAL ? (n_qtiles - 1 - wg / BH) : (wg / BH);
+    const int bh = wg % BH;
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+
+    const int q0 = qt * PF_BM;
+    const int wrow0 = q0 + wave * 32;
+    const int myrow = wrow0 + l32;
+    const bool wave_active = wrow0 < N;
+
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 w = buf_ld16(qrs, (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2);
+        if (negate) w = neg_bf16x8(w);
+        qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    const int row_end = min(q0 + PF_BM, N);
+    const int n_kt = CAUSAL ? (row_end + PF_BN - 1) / PF_BN : (N + PF_BN - 1) / PF_BN;
+    // this wave computes key tiles [0, my_kt)
+    const int my_kt = !wave_active ? 0 : (CAUSAL ? min(n_kt, (wrow0 + 31) / PF_BN + 1) : n_kt);
+
+    // Staging: unit p = (i * waves + wave) * 64 + lane holds the 16-byte
+    // chunk (row p / CPR, chunk (p % CPR) ^ swizzle(row)).  Successive i are
+    // 4096 bytes of rows apart and leave both swizzles unchanged, so one
+    // offset per lane and tensor serves every i (the rest is scalar).
+    uint32_t koff, voff;
+    {
+        const int p = wave * 64 + lane;
+        const int r = p / CPR;
+        koff = (uint32_t)(r * D + (((p % CPR) ^ kswz<CPR>(r)) * 8)) * 2;
+        voff = (uint32_t)(r * D + (((p % CPR) ^ vswz<CPR>(r)) * 8)) * 2;
+    }
+    constexpr uint32_t kInstBytes = PF_WAVES * 64 * 16;
+    auto load_k = [&](int kt, uint16_t* dst) {
+#pragma unroll
+        for (int i = 0; i < LINST; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + (i * PF_WAVES + wave) * 64 * 8), 16,
+                                                     koff, (uint32_t)kt * TILE * 2 + i * kInstBytes, 0, 0);
+    };
+    auto load_v = [&](int kt, uint16_t* dst) {
+#pragma unroll
+        for (int i = 0; i < LINST; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + (i * PF_WAVES + wave) * 64 * 8), 16,
+                                                     voff, (uint32_t)kt * TILE * 2 + i * kInstBytes, 0, 0);
+    };
+
+    // Operand read offsets (one opaque offset each, so every LDS read's
+    // address is a short chain from its array and the compiler can tell it
+    // apart from the loads in flight into the other buffers).
+    int kofs[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        int off = l32 * D + (((ks * 2 + hi) ^ kswz<CPR>(l32)) * 8);
+        asm("" : "+v"(off));
+        kofs[ks] = off;
+    }
+    int vofs[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        int off = pf_vtr_offset<D>(lane, db);
+        asm("" : "+v"(off));
+        vofs[db] = off;
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    // S^T = K Q^T of one tile (K operands three k-steps ahead of their MFMAs).
+    auto scores = [&](const uint16_t* Kb, f32x16 (&sacc)[2]) {
+        bf16x8 ka[KS][2];
+        auto kread = [&](int ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                ka[ks][kb] = *reinterpret_cast<const bf16x8*>(Kb + kofs[ks] + kb * 32 * D);
+        };
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        kread(0);
+        kread(1);
+        kread(2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 3 < KS) kread(ks + 3);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
+        }
+    };
+    // Row maximum of one tile, masked to -inf where not allowed.
+    auto rowmax = [&](f32x16 (&sacc)[2], int k0, auto mask_tag) -> float {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (MASK) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= myrow);
+                    sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+                }
+                mx = fmaxf(mx, sacc[kb][r]);
+            }
+        return max_halves(mx);
+    };
+    auto tile_mask = [&](int j) {
+        const int k0 = j * PF_BN;
+        return (k0 + PF_BN > N) || (CAUSAL && k0 + PF_BN - 1 > wrow0);
+    };
+    // Lazy rescale (as in the tile step): only when some row's maximum grew
+    // by more than 2^kLazyLog2, or on the first tile.
+    auto rescale = [&](float mx) {
+        const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+    };
+    // P = 2^(c s - c m) (masked scores are -inf and give exactly 0 since the
+    // launcher sends c = 0 to the plain kernel), row sum, bf16.
+    auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[4]) {
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        float lsum = 0.f;
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = fast_exp2(fmaf(sacc[c16 >> 1][(c16 & 1) * 8 + i], c, -mc));
+                lsum += p;
+                pb[c16][i] = (__bf16)p;
+            }
+        l_run += lsum;
+    };
+    // O^T += V^T P^T of one tile (V^T operands one key block ahead).
+    auto pv = [&](const uint16_t* Vb, const bf16x8 (&pb)[4]) {
+        bf16x8 va[2][NDB];
+        auto vread = [&](int c16, bf16x8* dst) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D));
+                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D + 8 * D));
+                dst[db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        vread(0, va[0]);
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16) {
+            if (c16 + 1 < 4) vread(c16 + 1, va[(c16 + 1) & 1]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c16 & 1][db], pb[c16], oacc[db], 0, 0, 0);
+        }
+    };
+
+    // Interleaving requests for the scheduler: the first LDS reads up front,
+    // then MFMAs spaced out with VALU (trans included) and the remaining LDS
+    // reads, so each read is issued several MFMAs before its use.
+    auto interleave = [](auto n_mfma_tag, auto valu_per_tag, auto ds_first_tag, auto ds_per_tag) {
+        constexpr int NM = decltype(n_mfma_tag)::value;
+        constexpr int NV = decltype(valu_per_tag)::value;
+        __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_first_tag)::value, 0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);  // VALU + trans
+            __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_tag)::value, 0);   // LDS reads
+        }
+    };
+    using MaskOn = std::true_type;
+    using MaskOff = std::false_type;
+
+    f32x16 sa[2], sb[2];
+    float mxa = kNegInf, mxb = kNegInf;
+
+    // Prologue: K(0), K(1), V(0) resident; scores and maximum of tile 0.
+    load_k(0, kbuf0);
+    if (n_kt > 1) load_k(1, kbuf1);
+    load_v(0, vbuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (my_kt > 0) {
+        scores(kbuf0, sa);
+        mxa = tile_mask(0) ? rowmax(sa, 0, MaskOn{}) : rowmax(sa, 0, MaskOff{});
+    }
+    __syncthreads();     // every wave's reads of K(0) precede the load into its buffer
+
+    // Iteration j: K(j+1) in kn, V(j) in vc; loads of K(j+2) into kd and
+    // V(j+1) into vd (their previous tiles were last read in iteration j-1).
+    auto iter = [&](int j, const uint16_t* kn, const uint16_t* vc, uint16_t* kd, uint16_t* vd,
+                    f32x16 (&scur)[2], f32x16 (&snxt)[2], float& mcur, float& mnxt) {
+        if (j + 2 < n_kt) load_k(j + 2, kd);
+        if (j + 1 < n_kt) load_v(j + 1, vd);
+        if (j + 1 < my_kt) {
+            rescale(mcur);
+            const int k1 = (j + 1) * PF_BN;
+            // One straight-line path per mask case of tile j+1, so that each
+            // block is a single scheduling region.
+            auto body = [&](auto mask_tag, auto valu_b) {
+                bf16x8 pb[4];
+                // block A
+                scores(kn, snxt);
+                probs(scur, pb);
+                interleave(std::integral_constant<int, 2 * KS>{}, std::integral_constant<int, 7>{},
+                           std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
+                __builtin_amdgcn_sched_barrier(0);
+                // block B
+                pv(vc, pb);
+                mnxt = rowmax(snxt, k1, mask_tag);
+                interleave(std::integral_constant<int, 16>{}, valu_b,
+                           std::integral_constant<int, 12>{}, std::integral_constant<int, 2>{});
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            if (tile_mask(j + 1))
+                body(MaskOn{}, std::integral_constant<int, 6>{});
+            else
+                body(MaskOff{}, std::integral_constant<int, 2>{});
+        } else if (j < my_kt) {
+            rescale(mcur);
+            bf16x8 pb[4];
+            probs(scur, pb);
+            pv(vc, pb);
+        }
+        __builtin_amdgcn_s_waitcnt(0);     // K(j+2), V(j+1) in LDS
+        __syncthreads();
+    };
+    for (int j = 0; j < n_kt; j += 2) {
+        iter(j, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb, mxa, mxb);
+        if (j + 1 < n_kt) iter(j + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa, mxb, mxa);
+    }
+
+    // Epilogue: o = u / l, lse = m + ln l (natural log).
+    const float l_tot = l_run + xor_shfl(l_run, 32);
+    if (wave_active && myrow < N) {
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        uint16_t* orow = o + ((size_t)bh * N + myrow) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int dim0 = db * 32 + rg * 8 + hi * 4;
+                const u32x2 w = {pack_bf16x2(oacc[db][rg * 4 + 0] * inv, oacc[db][rg * 4 + 1] * inv),
+                                 pack_bf16x2(oacc[db][rg * 4 + 2] * inv, oacc[db][rg * 4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + dim0) = w;
+            }
+        if (lse != nullptr && hi == 0) lse[(size_t)bh * N + myrow] = (m_run * c + log2f(l_tot)) * kLn2;
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.Hq;
     const int n_qt = (a.N + PF_BM - 1) / PF_BM;
     const dim3 grid((unsigned)(BH * n_qt)), block(PF_THREADS);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                       a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+    // The software-pipelined kernel for causal d = 128 (the long prefills);
+    // the plain one elsewhere: at d = 64 on short sequences it is faster, and
+    // the non-causal d = 128 build of the pipelined loop runs out of registers.
+    // Scale 0 also takes the plain kernel: the pipelined one relies on
+    // 2^(c * -inf - c m) being 0 for masked keys, which needs c > 0.
+    bool pipelined = false;
+    if constexpr (D == 128 && CAUSAL) pipelined = a.c > 0.f;
+    if (pipelined)
+        hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
     return hipGetLastError();
 }
 

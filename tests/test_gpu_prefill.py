@@ -52,16 +52,17 @@ def test_gqa_batches(dtype, B, Hq, Hkv, N, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
-def test_unusual_scales(dtype, scale):
+def test_unusual_scales(dtype, d, scale):
     """Scales far from 1/sqrt(d).  For fp32 the 1e-5 bound of the 1/sqrt(64)
-    workload is scaled by |scale| / 0.125: an fp32 dot product carries a
-    rounding error of order sqrt(d) * 2^-24 * |q||k|, and the softmax weights
-    see it multiplied by the scale."""
-    q, k, v = dense_inputs(B=1, Hq=2, Hkv=2, N=150, d=64, dtype=dtype, seed=31)
+    workload is scaled by |scale| / 0.125 and by sqrt(d / 64): an fp32 dot
+    product carries a rounding error of order sqrt(d) * 2^-24 * |q||k|, and the
+    softmax weights see it multiplied by the scale."""
+    q, k, v = dense_inputs(B=1, Hq=2, Hkv=2, N=150, d=d, dtype=dtype, seed=31)
     tol = O_TOL[DT[dtype]]
     if dtype == "f32":
-        tol *= max(1.0, abs(scale) / 0.125)
+        tol *= max(1.0, abs(scale) / 0.125) * math.sqrt(d / 64)
     for causal in (False, True):
         o, lse = run_fwd(q, k, v, scale, causal)
         ro, rl = OA.attention(f64(q), f64(k), f64(v), scale, causal)
@@ -116,11 +117,12 @@ def test_worked_example_across_tiles(dtype, reverse):
 # ------------------------------------------------------ closed forms ----
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_uniform_scores(dtype, causal):
+def test_uniform_scores(dtype, d, causal):
     """scale 0: o_i is the mean of the allowed values (a prefix mean when
     causal) and lse_i = ln(#allowed)."""
-    N, d = 200, 64
+    N = 200
     q, k, v = dense_inputs(B=1, Hq=2, Hkv=1, N=N, d=d, dtype=dtype, seed=3)
     o, lse = run_fwd(q, k, v, 0.0, causal)
     vv = f64(v)[0, 0]
