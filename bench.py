@@ -391,7 +391,7 @@ def main(argv=None):
                                                  ["prefill_bf16.hip", "prefill_tile.h", "common.h",
                                                   "internal.h"]),
                      "algorithmic_bytes": prefill_bytes(pcfg),
-                     "kernel": "prefill_bf16_kernel<128, causal>",
+                     "kernel": "prefill_sp_kernel<128, causal>",
                      "per_launch": {"flops": pf, "avg_us": round(pre_avg * 1e3, 2),
                                     "median_us": round(float(np.median(pre_ms)) * 1e3, 2),
                                     "min_us": round(min(pre_ms) * 1e3, 2)}},
