@@ -488,18 +488,19 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // the non-causal d = 128 build of the pipelined loop runs out of registers.
     // Scale 0 also takes the plain kernel: the pipelined one relies on
     // 2^(c * -inf - c m) being 0 for masked keys, which needs c > 0.
-    bool pipelined = false;
-    if constexpr (D == 128 && CAUSAL) pipelined = a.c > 0.f;
-    if (pipelined)
-        hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
-    else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+    if constexpr (D == 128 && CAUSAL) {
+        if (a.c > 0.f) {
+            hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                               a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                       a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
     return hipGetLastError();
 }
 
