@@ -287,119 +287,11 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    // S^T = K Q^T of one tile (K operands three k-steps ahead of their MFMAs).
-    auto scores = [&](const uint16_t* Kb, f32x16 (&sacc)[2]) {
-        bf16x8 ka[KS][2];
-        auto kread = [&](int ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                ka[ks][kb] = *reinterpret_cast<const bf16x8*>(Kb + kofs[ks] + kb * 32 * D);
-        };
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        kread(0);
-        kread(1);
-        kread(2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 3 < KS) kread(ks + 3);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
-        }
-    };
-    // Row maximum of one tile, masked to -inf where not allowed.
-    auto rowmax = [&](f32x16 (&sacc)[2], int k0, auto mask_tag) -> float {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (MASK) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool ok = key < N && (!CAUSAL || key <= myrow);
-                    sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
-                }
-                mx = fmaxf(mx, sacc[kb][r]);
-            }
-        return max_halves(mx);
-    };
+    const PfPipe<D, CAUSAL> pp{qf, kofs, vofs, oacc, m_run, l_run, c, hi, N, myrow};
     auto tile_mask = [&](int j) {
         const int k0 = j * PF_BN;
         return (k0 + PF_BN > N) || (CAUSAL && k0 + PF_BN - 1 > wrow0);
     };
-    // Lazy rescale (as in the tile step): only when some row's maximum grew
-    // by more than 2^kLazyLog2, or on the first tile.
-    auto rescale = [&](float mx) {
-        const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-        }
-    };
-    // P = 2^(c s - c m) (masked scores are -inf and give exactly 0 since the
-    // launcher sends c = 0 to the plain kernel), row sum, bf16.
-    auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[4]) {
-        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-        float lsum = 0.f;
-#pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = fast_exp2(fmaf(sacc[c16 >> 1][(c16 & 1) * 8 + i], c, -mc));
-                lsum += p;
-                pb[c16][i] = (__bf16)p;
-            }
-        l_run += lsum;
-    };
-    // O^T += V^T P^T of one tile (V^T operands one key block ahead).
-    auto pv = [&](const uint16_t* Vb, const bf16x8 (&pb)[4]) {
-        bf16x8 va[2][NDB];
-        auto vread = [&](int c16, bf16x8* dst) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D));
-                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D + 8 * D));
-                dst[db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        };
-        vread(0, va[0]);
-#pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16) {
-            if (c16 + 1 < 4) vread(c16 + 1, va[(c16 + 1) & 1]);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c16 & 1][db], pb[c16], oacc[db], 0, 0, 0);
-        }
-    };
-
-    // Interleaving requests for the scheduler: the first LDS reads up front,
-    // then MFMAs spaced out with VALU (trans included) and the remaining LDS
-    // reads, so each read is issued several MFMAs before its use.
-    auto interleave = [](auto n_mfma_tag, auto valu_per_tag, auto ds_first_tag, auto ds_per_tag) {
-        constexpr int NM = decltype(n_mfma_tag)::value;
-        constexpr int NV = decltype(valu_per_tag)::value;
-        __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_first_tag)::value, 0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);  // VALU + trans
-            __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_tag)::value, 0);   // LDS reads
-        }
-    };
-    using MaskOn = std::true_type;
-    using MaskOff = std::false_type;
 
     f32x16 sa[2], sb[2];
     float mxa = kNegInf, mxb = kNegInf;
@@ -411,8 +303,8 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (my_kt > 0) {
-        scores(kbuf0, sa);
-        mxa = tile_mask(0) ? rowmax(sa, 0, MaskOn{}) : rowmax(sa, 0, MaskOff{});
+        pp.scores(kbuf0, sa);
+        mxa = tile_mask(0) ? pp.template rowmax<true>(sa, 0) : pp.template rowmax<false>(sa, 0);
     }
     __syncthreads();     // every wave's reads of K(0) precede the load into its buffer
 
@@ -423,34 +315,33 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         if (j + 2 < n_kt) load_k(j + 2, kd);
         if (j + 1 < n_kt) load_v(j + 1, vd);
         if (j + 1 < my_kt) {
-            rescale(mcur);
+            pp.rescale(mcur);
             const int k1 = (j + 1) * PF_BN;
             // One straight-line path per mask case of tile j+1, so that each
             // block is a single scheduling region.
-            auto body = [&](auto mask_tag, auto valu_b) {
+            auto body = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
                 bf16x8 pb[4];
                 // block A
-                scores(kn, snxt);
-                probs(scur, pb);
-                interleave(std::integral_constant<int, 2 * KS>{}, std::integral_constant<int, 7>{},
-                           std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
+                pp.scores(kn, snxt);
+                pp.probs(scur, pb);
+                pf_interleave<2 * KS, 7, 6, 1>();
                 __builtin_amdgcn_sched_barrier(0);
                 // block B
-                pv(vc, pb);
-                mnxt = rowmax(snxt, k1, mask_tag);
-                interleave(std::integral_constant<int, 16>{}, valu_b,
-                           std::integral_constant<int, 12>{}, std::integral_constant<int, 2>{});
+                pp.pv(vc, pb);
+                mnxt = pp.template rowmax<MASK>(snxt, k1);
+                pf_interleave<16, MASK ? 6 : 2, 12, 2>();
                 __builtin_amdgcn_sched_barrier(0);
             };
             if (tile_mask(j + 1))
-                body(MaskOn{}, std::integral_constant<int, 6>{});
+                body(std::true_type{});
             else
-                body(MaskOff{}, std::integral_constant<int, 2>{});
+                body(std::false_type{});
         } else if (j < my_kt) {
-            rescale(mcur);
+            pp.rescale(mcur);
             bf16x8 pb[4];
-            probs(scur, pb);
-            pv(vc, pb);
+            pp.probs(scur, pb);
+            pp.pv(vc, pb);
         }
         __builtin_amdgcn_s_waitcnt(0);     // K(j+2), V(j+1) in LDS
         __syncthreads();

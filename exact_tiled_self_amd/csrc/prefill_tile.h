@@ -224,4 +224,132 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     }
 }
 
+// Pieces of the software-pipelined tile loop (prefill_sp_kernel, the dense
+// causal d = 128 prefill): one wave's 32 rows in the same layout as
+// pf_tile_step, with the wave's state held by reference.  Key `key` of a tile
+// is allowed for this lane's row iff key < kend and (when CAUSAL) key <= mypos.
+// The caller places the pieces so that the vector work of one tile sits
+// between the MFMAs of another (pf_interleave), because a wave's own
+// independent VALU instructions issue while its MFMAs execute.
+template <int D, bool CAUSAL>
+struct PfPipe {
+    static constexpr int KS = D / 16, NDB = D / 32;
+    const bf16x8 (&qf)[KS];
+    const int (&kofs)[KS];     // K operand offsets (rows l32, per k-step) inside a K tile
+    const int (&vofs)[NDB];    // V^T transpose-load offsets per dims block inside a V tile
+    f32x16 (&oacc)[NDB];
+    float& m_run;
+    float& l_run;
+    float c;
+    int hi, kend, mypos;
+
+    // S^T = K Q^T of one tile (K operands three k-steps ahead of their MFMAs).
+    __device__ __forceinline__ void scores(const uint16_t* Kb, f32x16 (&sacc)[2]) const {
+        bf16x8 ka[KS][2];
+        auto kread = [&](int ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                ka[ks][kb] = *reinterpret_cast<const bf16x8*>(Kb + kofs[ks] + kb * 32 * D);
+        };
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        kread(0);
+        kread(1);
+        kread(2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 3 < KS) kread(ks + 3);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
+        }
+    }
+    // Row maximum of one tile of keys k0 .., masked to -inf where not allowed.
+    template <bool MASK>
+    __device__ __forceinline__ float rowmax(f32x16 (&sacc)[2], int k0) const {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (MASK) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool ok = key < kend && (!CAUSAL || key <= mypos);
+                    sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+                }
+                mx = fmaxf(mx, sacc[kb][r]);
+            }
+        return max_halves(mx);
+    }
+    // Lazy rescale (as in pf_tile_step): only when some row's maximum grew by
+    // more than 2^kLazyLog2, or on the first tile.
+    __device__ __forceinline__ void rescale(float mx) const {
+        const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+    }
+    // P = 2^(c s - c m), row sum, bf16.  Masked scores are -inf and give
+    // exactly 0 only for c > 0: callers send c = 0 elsewhere.
+    __device__ __forceinline__ void probs(const f32x16 (&sacc)[2], bf16x8 (&pb)[4]) const {
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        float lsum = 0.f;
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = fast_exp2(fmaf(sacc[c16 >> 1][(c16 & 1) * 8 + i], c, -mc));
+                lsum += p;
+                pb[c16][i] = (__bf16)p;
+            }
+        l_run += lsum;
+    }
+    // O^T += V^T P^T of one tile (V^T operands one key block ahead).
+    __device__ __forceinline__ void pv(const uint16_t* Vb, const bf16x8 (&pb)[4]) const {
+        bf16x8 va[2][NDB];
+        auto vread = [&](int c16, bf16x8* dst) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D));
+                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vb + vofs[db] + c16 * 16 * D + 8 * D));
+                dst[db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        vread(0, va[0]);
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16) {
+            if (c16 + 1 < 4) vread(c16 + 1, va[(c16 + 1) & 1]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c16 & 1][db], pb[c16], oacc[db], 0, 0, 0);
+        }
+    }
+};
+
+// Interleaving request for the scheduler over the current region: D0 LDS
+// reads up front, then NM times one MFMA, NV VALU instructions (trans
+// included) and DP LDS reads, so each read is issued several MFMAs before its
+// use and the vector work fills the MFMAs' shadow.
+template <int NM, int NV, int D0, int DP>
+__device__ __forceinline__ void pf_interleave() {
+    __builtin_amdgcn_sched_group_barrier(0x100, D0, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);   // VALU + trans
+        __builtin_amdgcn_sched_group_barrier(0x100, DP, 0);   // LDS reads
+    }
+}
+
 }  // namespace attn
