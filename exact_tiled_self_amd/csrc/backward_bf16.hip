@@ -29,6 +29,8 @@
 // Causal tiles entirely outside the triangle are never visited; the heaviest
 // tiles are dispatched first.
 
+#include <type_traits>
+
 #include "internal.h"
 #include "prefill_tile.h"
 
@@ -218,16 +220,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             // dS^T = P^T (dP^T - D), P^T = 2^(c s - lse2); key of entry r:
             // k0 + 8(r/4) + 4hi + r%4.
             const bool need_mask = (k0 + BW_T > N) || (CAUSAL && k0 + BW_T - 1 > wrow0);
+            auto weights = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(sacc[r], c, -lse2));
-                if (need_mask) {
-                    const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool ok = key < N && (!CAUSAL || key <= myrow);
-                    p = ok ? p : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(sacc[r], c, -lse2));
+                    if (MASK) {
+                        const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        const bool ok = key < N && (!CAUSAL || key <= myrow);
+                        p = ok ? p : 0.f;
+                    }
+                    sacc[r] = p * (pacc[r] - drow);
                 }
-                sacc[r] = p * (pacc[r] - drow);
-            }
+            };
+            if (need_mask)
+                weights(std::true_type{});
+            else
+                weights(std::false_type{});
             // dQ^T += K^T dS^T, 16 keys per MFMA; K^T by transpose loads.
 #pragma unroll
             for (int c16 = 0; c16 < BW_T / 16; ++c16) {
@@ -405,26 +414,35 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
                 }
             }
-            const bool need_mask = (qc + BW_T > N) || (mykey >= N) ||
+            // wave-uniform (wkey0 is scalar), so the choice is one branch
+            // per chunk, not a masked region per element
+            const bool need_mask = (qc + BW_T > N) || (wkey0 + 31 >= N) ||
                                    (CAUSAL && qc < wkey0 + 31);
+            auto weights = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
-                f32x4 d4;
-                if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + 64 + 8 * rg + 4 * hi);
+                for (int rg = 0; rg < 4; ++rg) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
+                    f32x4 d4;
+                    if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + 64 + 8 * rg + 4 * hi);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rg * 4 + i;
-                    float p = fast_exp2(fmaf(sacc[r], c, -l4[i] * kLog2e));
-                    if (need_mask) {
-                        const int qi = qc + 8 * rg + 4 * hi + i;
-                        const bool ok = qi < N && mykey < N && (!CAUSAL || mykey <= qi);
-                        p = ok ? p : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rg * 4 + i;
+                        float p = fast_exp2(fmaf(sacc[r], c, -l4[i] * kLog2e));
+                        if (MASK) {
+                            const int qi = qc + 8 * rg + 4 * hi + i;
+                            const bool ok = qi < N && mykey < N && (!CAUSAL || mykey <= qi);
+                            p = ok ? p : 0.f;
+                        }
+                        if constexpr (MODE == kDK) p *= pacc[r] - d4[i];
+                        sacc[r] = p;
                     }
-                    if constexpr (MODE == kDK) p *= pacc[r] - d4[i];
-                    sacc[r] = p;
                 }
-            }
+            };
+            if (need_mask)
+                weights(std::true_type{});
+            else
+                weights(std::false_type{});
             // dV^T += dO^T P, or dK^T += Q^T dS: 16 queries per MFMA, the
             // transposed operand by transpose loads from the row-major tile.
             const uint16_t* At = base + (MODE == kDV ? St::GRM : St::QRM);
