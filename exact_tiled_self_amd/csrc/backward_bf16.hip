@@ -209,13 +209,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+            // K and V operands read two k-steps ahead of their MFMAs (the
+            // scheduling barriers keep the reads from sinking to their uses)
+            bf16x8 ka[D / 16], va[D / 16];
+            auto rd = [&](int ks) {
+                const int e = bw_rm<D>(l32, ks * 2 + hi);
+                ka[ks] = *reinterpret_cast<const bf16x8*>(Ks + e);
+                va[ks] = *reinterpret_cast<const bf16x8*>(Vs + e);
+            };
+            rd(0);
+            rd(1);
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int e = bw_rm<D>(l32, ks * 2 + hi);
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + e);
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + e);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], pacc, 0, 0, 0);
+                if (ks + 2 < D / 16) rd(ks + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], gf[ks], pacc, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // dS^T = P^T (dP^T - D), P^T = 2^(c s - lse2); key of entry r:
             // k0 + 8(r/4) + 4hi + r%4.
@@ -404,15 +414,25 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+            // Q (and dO) operands read KPF k-steps ahead of their MFMAs; the
+            // dK pass has no registers to spare for more than one
+            constexpr int KPF = MODE == kDV ? 3 : 1;
+            bf16x8 qa[D / 16], ga[D / 16];
+            auto rd = [&](int ks) {
+                const int e = bw_rm<D>(l32, ks * 2 + hi);
+                qa[ks] = *reinterpret_cast<const bf16x8*>(base + St::QRM + e);
+                if constexpr (MODE == kDK) ga[ks] = *reinterpret_cast<const bf16x8*>(base + St::GRM + e);
+            };
+#pragma unroll
+            for (int ks = 0; ks < KPF; ++ks) rd(ks);
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int e = bw_rm<D>(l32, ks * 2 + hi);
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(base + St::QRM + e);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-                if constexpr (MODE == kDK) {
-                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(base + St::GRM + e);
-                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], pacc, 0, 0, 0);
-                }
+                if (ks + KPF < D / 16) rd(ks + KPF);
+                __builtin_amdgcn_sched_barrier(0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sacc, 0, 0, 0);
+                if constexpr (MODE == kDK)
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], pacc, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // wave-uniform (wkey0 is scalar), so the choice is one branch
             // per chunk, not a masked region per element
