@@ -38,6 +38,8 @@
 // phases in order (tile step in prefill_tile.h); prefill_sp_kernel, used for
 // causal d = 128, software-pipelines them inside each wave (see its comment).
 
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "internal.h"
@@ -380,7 +382,10 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // Scale 0 also takes the plain kernel: the pipelined one relies on
     // 2^(c * -inf - c m) being 0 for masked keys, which needs c > 0.
     if constexpr (D == 128 && CAUSAL) {
-        if (a.c > 0.f) {
+        // ATTN_PREFILL_PLAIN=1 (test hook) keeps the plain kernel, so tests
+        // can compare the two
+        const char* plain = getenv("ATTN_PREFILL_PLAIN");
+        if (a.c > 0.f && !(plain != nullptr && plain[0] == '1')) {
             hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
