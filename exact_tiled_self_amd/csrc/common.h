@@ -83,14 +83,20 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
 }
 
 // max(x of this lane, x of lane l ^ 32) with v_permlane32_swap, a VALU
-// exchange between the two 32-lane halves of the wave (no LDS traffic).  With
-// the same register as both operands, one result holds the lower half's
-// values in both halves' positions swapped in and the other the upper half's,
-// so their maximum is the pairwise maximum in every lane.
+// exchange between the two 32-lane halves of the wave (no LDS traffic).  The
+// instruction swaps the upper half of its first register with the lower half
+// of its second: given x in both, the first ends up holding the lower half's
+// values in both halves and the second the upper half's, so their maximum is
+// the pairwise maximum in every lane.  Written as inline asm because the
+// compiler's builtin for it returns the first register as both results (so a
+// maximum of the two would silently be the lower half's value alone); the
+// s_nop pairs cover the VALU hazards around the instruction, which the
+// compiler cannot see inside the asm.  The instruction only moves register
+// values between lanes.
 __device__ __forceinline__ float max_halves(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // Hardware base-2 exponential (v_exp_f32).

@@ -267,6 +267,30 @@ def test_pipelined_matches_plain(monkeypatch, B, Hq, Hkv, N):
     assert max_abs(f64(o1), ro) <= O_TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("spike", [4, 84])
+def test_row_max_spans_both_lane_halves(d, causal, spike):
+    """The row maximum must cover all keys of a tile.  In the transposed score
+    layout the keys at positions 4..7 (mod 8) of each block sit in the upper
+    32 lanes; put the only large score there, far enough above the rest that a
+    maximum taken over the lower lanes alone would overflow 2^(c (s - m))
+    (here c s ~ 277), and the output must still be that key's value row."""
+    N = 200
+    g = torch.Generator().manual_seed(spike + d)
+    q = torch.zeros(1, 1, N, d)
+    k = torch.zeros(1, 1, N, d)
+    q[..., 0] = 8.0
+    k[0, 0, spike, 0] = 16.0
+    v = torch.randn(1, 1, N, d, generator=g)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, lse = run_fwd(q, k, v, 1.5, causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), 1.5, causal)
+    assert max_abs(f64(o), ro) <= O_TOL[torch.bfloat16]
+    assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
+
+
 def test_no_lse_output():
     q, k, v = dense_inputs(B=1, Hq=2, Hkv=1, N=100, d=64, dtype="bf16", seed=2)
     o1, _ = run_fwd(q, k, v, 0.125, True, want_lse=False)
