@@ -118,6 +118,38 @@ def test_spike_through_block_table():
                 assert err <= 1e-2, (rep, s, h, err)
 
 
+def test_row_max_spans_all_lane_groups():
+    """The decode's row maximum combines four 16-lane groups, each holding 4
+    of a block's 16 keys.  Put the only large score of a sequence in each group
+    in turn (slot 1, 6, 9, 14, ...), so far above the rest (c s ~ 277) that a
+    maximum missing that group would overflow 2^(c (s - m)); the output must
+    be exactly that key's value row."""
+    cfg = small_cfg(Hq=12, Hkv=2, d=128)
+    ctx = [16, 16, 16, 16, 40, 700]
+    spikes = [1, 6, 9, 14, 36, 699]            # slots 1, 6, 9, 14, 4, 11: every lane group
+    p = paged_inputs(cfg, S=len(ctx), ctx_lens=ctx, poison=True, extra_blocks=2,
+                     max_blocks=64, seed=21)
+    q = torch.zeros_like(p["q"], dtype=torch.float32)
+    q[..., 0] = 8.0
+    kc = p["k_cache"].float()
+    kc[..., 0] = torch.where(torch.isnan(kc[..., 0]), kc[..., 0], torch.zeros_like(kc[..., 0]))
+    t = p["block_table"].numpy()
+    targets = []
+    for s, ps in enumerate(spikes):
+        blk, slot = int(t[s, ps // 16]), ps % 16
+        kc[blk, :, slot, 0] = 16.0
+        targets.append(p["v_cache"][blk, :, slot].double())
+    p["q"] = q.to(torch.bfloat16)
+    p["k_cache"] = kc.to(torch.bfloat16)
+    o, lse = run_decode(p, 1.5)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for s in range(len(ctx)):
+        for h in range(12):
+            err = (o[s, h].double() - targets[s][h // 6]).abs().max().item()
+            assert err <= 1e-2, (s, h, err)
+    assert (lse.double() - 192.0).abs().max().item() <= LSE_TOL
+
+
 def test_identity_table_matches_dense():
     """A contiguous cache with an identity table is ordinary single-query
     attention: compare with the dense kernel on the same keys."""
