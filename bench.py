@@ -22,6 +22,11 @@ intermediate 8960): residual add + RMSNorm and the SwiGLU activation.
 Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+With `--configs NAME[,NAME...]` (or `--configs all`) it instead times
+attn_fwd alone on each named dense workload (the ViT-B/16 shapes, the GQA and
+the long MHA causal prefills) and prints one JSON line per workload: TFLOP/s
+against the MFMA peak of its dtype and algorithmic GB/s against the HBM peak.
 """
 
 from __future__ import annotations
@@ -40,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak; paged decode GB/s & % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector alike)
 
 
 def prefill_flops(cfg) -> float:
@@ -142,6 +148,75 @@ def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100):
                       f"T={cfg.N}, d={cfg.d}, causal), float64 numpy oracle on the host copy"}
 
 
+def plain_copy(torch, dev, mib):
+    """A plain streaming kernel of known size (reads and writes `mib` MiB once
+    each): torch's elementwise negation, not the runtime's blit copy."""
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_configs(names, steps, warmup, copy_mib=0):
+    """attn_fwd alone on each named dense workload: HIP events on the launch
+    stream around every call; one JSON line per workload."""
+    import torch
+    from exact_tiled_self_amd import attn_fwd
+    from exact_tiled_self_amd.inputs import DENSE_CONFIGS, dense_inputs
+
+    if names == ["all"]:
+        names = list(DENSE_CONFIGS)
+    unknown = [n for n in names if n not in DENSE_CONFIGS]
+    if unknown:
+        raise SystemExit(f"unknown workload(s) {unknown}; known: {sorted(DENSE_CONFIGS)}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    if copy_mib > 0:
+        plain_copy(torch, dev, copy_mib)
+    for name in names:
+        cfg = DENSE_CONFIGS[name]
+        q, k, v = (t.to(dev) for t in dense_inputs(cfg))
+        o = torch.empty_like(q)
+        lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device=dev)
+
+        def fwd():
+            attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, o=o, lse=lse, stream=stream)
+
+        for _ in range(warmup):
+            fwd()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for i in range(steps):
+            fwd()
+            e[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [e[i].elapsed_time(e[i + 1]) for i in range(steps)]
+        avg_s = float(np.mean(ms)) / 1e3
+        fl, by = prefill_flops(cfg), prefill_bytes(cfg)
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        if cfg.dtype == "f32":
+            kernel = f"prefill_f32_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
+        elif cfg.d == 128 and cfg.causal:
+            kernel = f"prefill_sp_kernel<{cfg.d}, causal>"
+        else:
+            kernel = f"prefill_bf16_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
+        print(json.dumps({
+            "workload": name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
+            "dtype": cfg.dtype, "causal": cfg.causal, "steps": steps, "warmup": warmup,
+            "avg_us": round(avg_s * 1e6, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+            "min_us": round(min(ms) * 1e3, 2),
+            "TFLOP/s": round(fl / avg_s / 1e12, 2), "frac_mfma": round(fl / avg_s / 1e12 / peak, 4),
+            "mfma_peak_TFLOP/s": peak, "GB/s": round(by / avg_s / 1e9, 1),
+            "frac_hbm": round(by / avg_s / 1e9 / PEAK_HBM_GBPS, 4),
+            "flops": fl, "algorithmic_bytes": int(by), "kernel": kernel}), flush=True)
+        del q, k, v, o, lse
+    return 0
+
+
 def read_clocks():
     """sclk / mclk lines of `rocm-smi --showclocks` (run as a child process right
     after the timed loop), or None when the tool is unavailable."""
@@ -168,12 +243,18 @@ def main(argv=None):
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--configs", default=None,
+                    help="comma-separated dense workloads (or 'all'): time attn_fwd alone on each "
+                         "and print one JSON line per workload instead of the bench line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
+
+    if args.configs:
+        return run_configs(args.configs.split(","), args.steps, args.warmup, args.copy_mib)
 
     import torch
     from exact_tiled_self_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
@@ -207,14 +288,7 @@ def main(argv=None):
                           16, dcfg.scale, o=od, lse=lsed, workspace=ws, stream=stream)
 
     if args.copy_mib > 0:
-        # a plain streaming kernel of known size (reads and writes copy_mib MiB
-        # once each): torch's elementwise negation, not the runtime's blit copy
-        src = torch.ones((args.copy_mib << 20) // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        plain_copy(torch, dev, args.copy_mib)
 
     for _ in range(args.warmup):
         prefill()

@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                     float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
-                    float c, int negate) {
+                    float c, int negate, int xcd_runs) {
     using L = PfLayout<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem0[L::BUF];
     __shared__ __attribute__((aligned(16))) uint16_t smem1[L::BUF];
@@ -64,8 +64,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     // Work unit: (b, h, q tile); heaviest q tiles first when causal.
     const int wg = blockIdx.x;
-    const int qt = CAUSAL ? (n_qtiles - 1 - wg / BH) : (wg / BH);
-    const int bh = wg % BH;
+    int qt, bh;
+    if (!CAUSAL && xcd_runs) {
+        // Workgroup w runs on XCD w % 8.  A run is the G * n_qtiles units
+        // that read one kv head's K and V; run r goes to XCD r % 8, and the
+        // j-th workgroup of XCD x takes unit j % (run length) of run
+        // (j / run length) * 8 + x, so a run's units follow each other on
+        // one XCD and the K/V tiles they share stay in its L2.  The grid is
+        // padded to whole rounds of 8 runs; padding workgroups exit here.
+        const int G = Hq / Hkv, R = G * n_qtiles;
+        const int x = wg & 7, j = wg >> 3;
+        const int r = (j / R) * 8 + x;
+        if (r >= BH / G) return;
+        const int i = j - (j / R) * R;
+        qt = i / G;
+        bh = r * G + (i - qt * G);
+    } else {
+        qt = CAUSAL ? (n_qtiles - 1 - wg / BH) : (wg / BH);
+        bh = wg % BH;
+    }
     const int b = bh / Hq, h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
     const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -393,10 +410,18 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+    // Non-causal: XCD-local runs of the units that share a kv head (grid
+    // padded to whole rounds of 8 runs), when the runs spread evenly over the
+    // 8 XCDs (a multiple of 8 runs, or enough that one extra run per XCD
+    // matters little) and the padded grid fits.
+    const long long runs = (long long)BH / (a.Hq / a.Hkv);
+    const long long padded = (runs + 7) / 8 * 8 * (a.Hq / a.Hkv) * n_qt;
+    const int xcd_runs = (!CAUSAL && (runs % 8 == 0 || runs >= 128) && padded < (1LL << 31)) ? 1 : 0;
+    const dim3 grid_p(xcd_runs ? (unsigned)padded : grid.x);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid_p, block, 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                       a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+                       a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate, xcd_runs);
     return hipGetLastError();
 }
 

@@ -268,6 +268,19 @@ def test_pipelined_matches_plain(monkeypatch, B, Hq, Hkv, N):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(8, 2, 1, 300), (4, 6, 2, 129), (2, 8, 8, 64), (1, 16, 8, 200)])
+def test_xcd_runs_cover_every_tile(d, B, Hq, Hkv, N):
+    """Non-causal launches with a multiple of 8 kv heads (over the batch) map
+    the q tiles that share a kv head to one XCD in a run; every (head, q tile)
+    must still be computed once, against its own kv head."""
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=90 + N + Hq)
+    o, lse = run_fwd(q, k, v, 1.0 / math.sqrt(d), False)
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(d), False)
+    assert max_abs(f64(o), ro) <= O_TOL[torch.bfloat16]
+    assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("spike", [4, 84])
 def test_row_max_spans_both_lane_halves(d, causal, spike):
