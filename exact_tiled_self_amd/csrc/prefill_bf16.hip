@@ -33,6 +33,9 @@
 //   * Causal: tiles entirely above the diagonal are never visited, the q
 //     tiles are dispatched heaviest first, and a wave whose rows all lie
 //     before a tile skips its arithmetic for it.
+//   * Non-causal: the q tiles that read one kv head run as consecutive
+//     workgroups of one XCD, so its K/V tiles come from HBM once and from
+//     that XCD's L2 after.
 //
 // Two kernels share this layout: prefill_bf16_kernel runs each key tile's
 // phases in order (tile step in prefill_tile.h); prefill_sp_kernel, used for
