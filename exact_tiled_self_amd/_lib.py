@@ -106,6 +106,26 @@ def _dev(t: torch.Tensor, name: str):
     return t.data_ptr()
 
 
+def _check_out(t, name: str, shape, dtype, ref: torch.Tensor):
+    """A caller-supplied output must be exactly what the kernels write: the
+    library receives only its pointer, so a smaller or differently typed
+    buffer would be written past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
+
+
+def _same_device(ref: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
+
+
 def _stream_ptr(device, stream):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -125,10 +145,15 @@ def attn_fwd(q, k, v, scale=None, causal=False, *, o=None, lse=None, want_lse=Tr
     Hkv = k.shape[1]
     if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    _same_device(q, k=k, v=v)
     if o is None:
         o = torch.empty_like(q)
+    else:
+        _check_out(o, "o", (B, Hq, N, d), q.dtype, q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out(lse, "lse", (B, Hq, N), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     ptrs = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
@@ -162,10 +187,16 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, ctx_lens, block_size=16,
             or tuple(ctx_lens.shape) != (S,):
         raise ValueError("inconsistent decode shapes")
     max_blocks = block_table.shape[1]
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, ctx_lens=ctx_lens,
+                 workspace=workspace)
     if o is None:
         o = torch.empty_like(q)
+    else:
+        _check_out(o, "o", (S, Hq, d), q.dtype, q)
     if lse is None and want_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out(lse, "lse", (S, Hq), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size)
@@ -206,6 +237,8 @@ def attn_kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_lens, starts
         raise ValueError("k_new and v_new must be [T, Hkv, d] matching the caches")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or k_cache.dtype not in _DTYPE:
         raise ValueError("new rows and caches must share dtype float32 or bfloat16")
+    _same_device(k_cache, k_new=k_new, v_new=v_new, v_cache=v_cache, block_table=block_table,
+                 ctx_lens=ctx_lens, starts=starts)
     T = k_new.shape[0]
     st = raw_library().attn_kv_append(
         _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -225,10 +258,16 @@ def attn_paged_prefill(q, k_cache, v_cache, block_table, ctx_lens, starts, block
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_cache.dtype or q.dtype not in _DTYPE:
         raise ValueError("q must be [T, Hq, d] with the caches' d and dtype")
     T, Hq = q.shape[0], q.shape[1]
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, ctx_lens=ctx_lens,
+                 starts=starts)
     if o is None:
         o = torch.empty_like(q)
+    else:
+        _check_out(o, "o", (T, Hq, d), q.dtype, q)
     if lse is None and want_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out(lse, "lse", (T, Hq), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = raw_library().attn_paged_prefill(
@@ -258,6 +297,10 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, *, dq=None, dk=Non
     Hkv = k.shape[1]
     if tuple(k.shape) != (B, Hkv, N, d) or tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
         raise ValueError("inconsistent shapes, or lse not float32 [B, Hq, N]")
+    _same_device(q, k=k, v=v, o=o, lse=lse, dout=dout, workspace=workspace)
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if t is not None:
+            _check_out(t, name, ref.shape, ref.dtype, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -283,6 +326,10 @@ def attn_add_rmsnorm(x, residual, weight, eps=1e-6, *, out=None, residual_out=No
         raise ValueError("x, residual must be [T, D] and weight [D]")
     if not (x.dtype == residual.dtype == weight.dtype) or x.dtype not in _DTYPE:
         raise ValueError("x, residual and weight must share dtype")
+    _same_device(x, residual=residual, weight=weight)
+    for t, name in ((out, "out"), (residual_out, "residual_out")):
+        if t is not None:
+            _check_out(t, name, x.shape, x.dtype, x)
     out = torch.empty_like(x) if out is None else out
     residual_out = torch.empty_like(x) if residual_out is None else residual_out
     T, D = x.shape
@@ -303,15 +350,17 @@ def attn_swiglu(gate, up=None, *, out=None, stream=None):
         if F2 % 2:
             raise ValueError("a merged gate/up tensor needs an even width")
         F, ld_in = F2 // 2, F2
-        g_ptr = _dev(gate, "gate")
-        u_ptr = g_ptr + F * gate.element_size()
     else:
         if up.shape != gate.shape or up.dtype != gate.dtype:
             raise ValueError("gate and up must match")
+        _same_device(gate, up=up)
         T, F = gate.shape
         ld_in = F
-        g_ptr, u_ptr = _dev(gate, "gate"), _dev(up, "up")
+    if out is not None:
+        _check_out(out, "out", (T, F), gate.dtype, gate)
     out = torch.empty((T, F), dtype=gate.dtype, device=gate.device) if out is None else out
+    g_ptr = _dev(gate, "gate")
+    u_ptr = g_ptr + F * gate.element_size() if up is None else _dev(up, "up")
     st = raw_library().attn_swiglu(g_ptr, u_ptr, _dev(out, "out"), T, F, ld_in, F, _DTYPE[gate.dtype],
                                    _stream_ptr(gate.device, stream))
     _check(st)

@@ -1,6 +1,8 @@
 """Build libattn.so in-tree with hipcc for gfx950.
 
     python -m exact_tiled_self_amd.build          # build (always recompiles)
+    python -m exact_tiled_self_amd.build --sanitize   # libattn_san.so: host code
+                                                      # under ASan + UBSan
 
 The library is written to exact_tiled_self_amd/libattn.so via a temporary
 file and an atomic rename, so a process that already loaded the old file is
@@ -21,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+SAN_LIB_PATH = os.path.join(PKG, "libattn_san.so")
 
 SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "prefill_paged.hip",
            "kv_append.hip", "backward_bf16.hip", "fusion.hip"]
@@ -43,6 +46,29 @@ EXTRA_FLAGS = {
 }
 
 
+# Host-only sanitizer build of the C ABI layer (argument checking, error
+# strings, architecture cache).  Every -fsanitize flag is bound to the host
+# pass; api.cpp holds no device code, and the kernels are built as usual.
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-shared-libsan",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_SOURCES = {"api.cpp"}
+
+
+def asan_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime, which a process that
+    loads the sanitized library must preload."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if not out or not os.path.isabs(out) or not os.path.exists(out):
+        import glob
+        hits = sorted(glob.glob("/opt/rocm*/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not hits:
+            raise RuntimeError("no shared AddressSanitizer runtime found")
+        out = hits[-1]
+    return out
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -50,9 +76,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, out: str = LIB_PATH) -> str:
+def build(verbose: bool = False, out: str | None = None, sanitize: bool = False) -> str:
     """Compile every source (in parallel, each with its own flags), link
-    them into `out` and return its path."""
+    them into `out` and return its path.  With `sanitize`, the host-side ABI
+    layer is built under AddressSanitizer and UndefinedBehaviorSanitizer into
+    libattn_san.so (by default)."""
+    if out is None:
+        out = SAN_LIB_PATH if sanitize else LIB_PATH
     from concurrent.futures import ThreadPoolExecutor
 
     noise = "is not a recognized feature for this target"   # hipcc host-pass noise
@@ -60,7 +90,8 @@ def build(verbose: bool = False, out: str = LIB_PATH) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC,
+            san = SAN_FLAGS if sanitize and src in SAN_SOURCES else []
+            cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *san, "-I", INCLUDE, "-I", CSRC,
                    "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -79,7 +110,8 @@ def build(verbose: bool = False, out: str = LIB_PATH) -> str:
                     print("\n".join(msgs))
         fd, tmp = tempfile.mkstemp(prefix=".libattn.", suffix=".so.tmp", dir=os.path.dirname(out))
         os.close(fd)
-        cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp, *[obj for _, obj, _, _ in results]]
+        cmd = [hipcc(), *HIP_FLAGS, *(SAN_FLAGS if sanitize else []), "-shared", "-o", tmp,
+               *[obj for _, obj, _, _ in results]]
         if verbose:
             print(" ".join(cmd), flush=True)
         proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -93,5 +125,5 @@ def build(verbose: bool = False, out: str = LIB_PATH) -> str:
 
 
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
+    path = build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv)
     print(path)

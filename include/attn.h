@@ -62,7 +62,13 @@ typedef enum {
 
 typedef enum {
     ATTN_F32 = 0,               /* IEEE binary32 in and out, fp32 arithmetic throughout */
-    ATTN_BF16 = 1               /* bfloat16 in and out, fp32 accumulation */
+    ATTN_BF16 = 1,              /* bfloat16 in and out, fp32 accumulation */
+    /* Not element types: these two bounds make every 32-bit int a valid value
+       of attn_dtype, so whatever a caller passes can be read and rejected
+       with ATTN_ERR_UNSUPPORTED (in C++ reading a value outside an enum's
+       range is undefined).  The type stays int-sized. */
+    ATTN_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    ATTN_DTYPE_RANGE_MAX_ = 0x7fffffff
 } attn_dtype;
 
 /*

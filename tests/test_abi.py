@@ -258,3 +258,74 @@ def test_binding_rejects_host_tensors():
         _lib.attn_fwd(q, q[:, :1], q[:, :1])
     with pytest.raises(ValueError):
         _lib.attn_fwd(q.to(torch.float16), q[:, :1], q[:, :1])
+
+
+# ---------------------------------------- binding: caller-supplied outputs ----
+# The C ABI receives only pointers, so the binding checks every output it is
+# handed against the shape and dtype the kernels write.  These checks run
+# before any pointer is taken, so host tensors show them without a GPU.
+
+def _expect_bad_output(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_rejects_wrong_fwd_outputs():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    _expect_bad_output(lambda: _lib.attn_fwd(q, k, k, o=torch.zeros(1, 4, 7, 64, dtype=torch.bfloat16)),
+                       "o must have shape")
+    _expect_bad_output(lambda: _lib.attn_fwd(q, k, k, o=torch.zeros(1, 4, 8, 64)), "o must have dtype")
+    _expect_bad_output(lambda: _lib.attn_fwd(q, k, k, lse=torch.zeros(1, 4, 8, dtype=torch.bfloat16)),
+                       "lse must have dtype")
+    _expect_bad_output(lambda: _lib.attn_fwd(q, k, k, lse=torch.zeros(1, 4, 9)), "lse must have shape")
+
+
+def test_binding_rejects_wrong_decode_outputs():
+    q = torch.zeros(3, 12, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(10, 2, 16, 128, dtype=torch.bfloat16)
+    tab = torch.zeros(3, 4, dtype=torch.int32)
+    ctx = torch.zeros(3, dtype=torch.int32)
+    _expect_bad_output(lambda: _lib.attn_paged_decode(q, kc, kc, tab, ctx, o=torch.zeros(3, 12, 64,
+                                                                                          dtype=torch.bfloat16)),
+                       "o must have shape")
+    _expect_bad_output(lambda: _lib.attn_paged_decode(q, kc, kc, tab, ctx, lse=torch.zeros(3, 12,
+                                                                                            dtype=torch.float64)),
+                       "lse must have dtype")
+
+
+def test_binding_rejects_wrong_paged_prefill_outputs():
+    q = torch.zeros(5, 12, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(10, 2, 16, 128, dtype=torch.bfloat16)
+    tab = torch.zeros(2, 4, dtype=torch.int32)
+    ctx = torch.zeros(2, dtype=torch.int32)
+    starts = torch.zeros(3, dtype=torch.int32)
+    _expect_bad_output(lambda: _lib.attn_paged_prefill(q, kc, kc, tab, ctx, starts,
+                                                       o=torch.zeros(4, 12, 128, dtype=torch.bfloat16)),
+                       "o must have shape")
+    _expect_bad_output(lambda: _lib.attn_paged_prefill(q, kc, kc, tab, ctx, starts,
+                                                       lse=torch.zeros(5, 12, dtype=torch.bfloat16)),
+                       "lse must have dtype")
+
+
+def test_binding_rejects_wrong_bwd_outputs():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 4, 8)
+    _expect_bad_output(lambda: _lib.attn_bwd(q, k, k, q, lse, q, dq=torch.zeros(1, 4, 8, 32, dtype=torch.bfloat16)),
+                       "dq must have shape")
+    _expect_bad_output(lambda: _lib.attn_bwd(q, k, k, q, lse, q, dk=torch.zeros_like(q)), "dk must have shape")
+    _expect_bad_output(lambda: _lib.attn_bwd(q, k, k, q, lse, q, dv=torch.zeros(1, 2, 8, 64)), "dv must have dtype")
+
+
+def test_binding_rejects_wrong_fusion_outputs():
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    w = torch.zeros(256, dtype=torch.bfloat16)
+    _expect_bad_output(lambda: _lib.attn_add_rmsnorm(x, x, w, out=torch.zeros(4, 128, dtype=torch.bfloat16)),
+                       "out must have shape")
+    _expect_bad_output(lambda: _lib.attn_add_rmsnorm(x, x, w, residual_out=torch.zeros(4, 256)),
+                       "residual_out must have dtype")
+    gu = torch.zeros(4, 512, dtype=torch.bfloat16)
+    _expect_bad_output(lambda: _lib.attn_swiglu(gu, out=torch.zeros(4, 512, dtype=torch.bfloat16)),
+                       "out must have shape")
+    _expect_bad_output(lambda: _lib.attn_swiglu(x, x, out=torch.zeros(4, 256)), "out must have dtype")
