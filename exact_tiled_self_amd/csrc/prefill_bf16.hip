@@ -51,13 +51,13 @@
 namespace attn {
 namespace {
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int BN>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                     float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
                     float c, int negate, int xcd_runs) {
-    using L = PfLayout<D>;
+    using L = PfLayout<D, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t smem0[L::BUF];
     __shared__ __attribute__((aligned(16))) uint16_t smem1[L::BUF];
 
@@ -109,7 +109,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     const int row_end = min(q0 + PF_BM, N);
-    const int n_kt = CAUSAL ? (row_end + PF_BN - 1) / PF_BN : (N + PF_BN - 1) / PF_BN;
+    const int n_kt = CAUSAL ? (row_end + BN - 1) / BN : (N + BN - 1) / BN;
 
     // K staging: load-to-LDS unit p = (i * waves + wave) * 64 + lane holds the
     // 16-byte chunk (row p / CPR, chunk (p % CPR) ^ swz(row)) of the tile.
@@ -132,7 +132,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     auto issue_loads = [&](int kt, uint16_t* Ks) {
-        const uint32_t t0 = (uint32_t)kt * PF_BN * D * 2;
+        const uint32_t t0 = (uint32_t)kt * BN * D * 2;
         uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
         for (int i = 0; i < L::KINST; ++i)
@@ -161,11 +161,11 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     auto step = [&](int kt, const uint16_t* cur, uint16_t* nxt) {
         const bool more = kt + 1 < n_kt;
         if (more) issue_loads(kt + 1, nxt);
-        const int k0 = kt * PF_BN;
+        const int k0 = kt * BN;
         const bool compute = wave_active && (!CAUSAL || k0 <= wrow0 + 31);
         if (compute) {
-            const bool need_mask = (k0 + PF_BN > N) || (CAUSAL && k0 + PF_BN - 1 > wrow0);
-            pf_tile_step<D, CAUSAL>(cur, cur + L::KELEMS, qf, oacc, m_run, l_run, k0, N, myrow,
+            const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wrow0);
+            pf_tile_step<D, CAUSAL, BN>(cur, cur + L::KELEMS, qf, oacc, m_run, l_run, k0, N, myrow,
                                     need_mask, c, hi, l32);
         }
         if (more) __builtin_amdgcn_s_waitcnt(0);     // tile kt+1 in LDS
@@ -401,11 +401,16 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // the non-causal d = 128 build of the pipelined loop runs out of registers.
     // Scale 0 also takes the plain kernel: the pipelined one relies on
     // 2^(c * -inf - c m) being 0 for masked keys, which needs c > 0.
+    // ATTN_PREFILL_BN=32 (test hook): the plain kernel with 32-key tiles, a
+    // second partition of the keys, which must give the same result within
+    // the tolerances.
+    const char* bn_env = getenv("ATTN_PREFILL_BN");
+    const bool bn32 = bn_env != nullptr && bn_env[0] == '3' && bn_env[1] == '2' && bn_env[2] == '\0';
     if constexpr (D == 128 && CAUSAL) {
         // ATTN_PREFILL_PLAIN=1 (test hook) keeps the plain kernel, so tests
         // can compare the two
         const char* plain = getenv("ATTN_PREFILL_PLAIN");
-        if (a.c > 0.f && !(plain != nullptr && plain[0] == '1')) {
+        if (a.c > 0.f && !bn32 && !(plain != nullptr && plain[0] == '1')) {
             hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
@@ -421,10 +426,16 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     const long long padded = (runs + 7) / 8 * 8 * (a.Hq / a.Hkv) * n_qt;
     const int xcd_runs = (!CAUSAL && (runs % 8 == 0 || runs >= 128) && padded < (1LL << 31)) ? 1 : 0;
     const dim3 grid_p(xcd_runs ? (unsigned)padded : grid.x);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid_p, block, 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                       a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate, xcd_runs);
+    if (bn32)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, 32>), grid_p, block, 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate, xcd_runs);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PF_BN>), grid_p, block, 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                           a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate, xcd_runs);
     return hipGetLastError();
 }
 

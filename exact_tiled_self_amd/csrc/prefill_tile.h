@@ -31,14 +31,15 @@ constexpr int PF_BM = 32 * PF_WAVES;   // query rows per workgroup
 constexpr int PF_BN = 64;              // keys per tile
 constexpr int PF_THREADS = 64 * PF_WAVES;
 
-template <int D>
+template <int D, int BN = PF_BN>
 struct PfLayout {
+    static_assert(BN == 32 || BN == 64, "key tiles of 32 or 64 keys");
     static constexpr int CPR = D / 8;           // 16-byte chunks per row
-    static constexpr int KELEMS = PF_BN * D;    // K tile, rows XOR-swizzled, no pad
-    static constexpr int VELEMS = PF_BN * D;    // V tile, the same shape
+    static constexpr int KELEMS = BN * D;       // K tile, rows XOR-swizzled, no pad
+    static constexpr int VELEMS = BN * D;       // V tile, the same shape
     static constexpr int BUF = KELEMS + VELEMS; // one pipeline stage (bf16 elements)
-    static constexpr int KINST = PF_BN * CPR / PF_THREADS;     // load-to-LDS per thread per tile
-    static_assert(KINST * PF_THREADS == PF_BN * CPR, "tile split");
+    static constexpr int KINST = BN * CPR / PF_THREADS;     // load-to-LDS per thread per tile
+    static_assert(KINST * PF_THREADS == BN * CPR, "tile split");
 };
 
 // XOR swizzle of the 16-byte chunks of K row r, so that the 16 rows read by
@@ -78,16 +79,17 @@ __device__ __forceinline__ int pf_vtr_offset(int lane, int db) {
 // numerator needs no rescale.  u / l is unchanged by the choice of reference.
 constexpr float kLazyLog2 = 8.0f;
 
-// Advance one wave's rows over the tile of keys k0 .. k0 + 63 staged at Ks
-// (K) and Vs (V, row-major).  Key position `key` is allowed for this lane's row iff
+// Advance one wave's rows over the tile of keys k0 .. k0 + BN - 1 staged at
+// Ks (K) and Vs (V, row-major).  BN (keys per tile) is 64, or 32 for a
+// second tile configuration (any partition of the keys gives the same u / l).  Key position `key` is allowed for this lane's row iff
 // key < kend and (when CAUSAL) key <= mypos; `need_mask` must be true
 // whenever some key of the tile fails that test for some row of the wave.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int BN = PF_BN>
 __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t* Vs, const bf16x8* qf,
                                              f32x16* oacc, float& m_run, float& l_run, int k0,
                                              int kend, int mypos, bool need_mask, float c, int hi,
                                              int l32) {
-    using L = PfLayout<D>;
+    using L = PfLayout<D, BN>;
     constexpr int KS = D / 16;           // k-steps of the score product
     constexpr int KPF = KS < 4 ? KS : 4; // K operand pairs read ahead of their MFMAs
     const int lane = hi * 32 + l32;
@@ -96,10 +98,10 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     // scheduling barriers keep the compiler from sinking them back to their
     // uses), so an LDS round trip overlaps the matrix work instead of
     // preceding every MFMA.
-    bf16x8 ka[KS][PF_BN / 32];
+    bf16x8 ka[KS][BN / 32];
     auto kread = [&](int ks) {
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
             const int r = kb * 32 + l32;
             const int cc = (ks * 2 + hi) ^ kswz<L::CPR>(r);
             ka[ks][kb] = *reinterpret_cast<const bf16x8*>(Ks + (r * D + cc * 8));
@@ -127,9 +129,9 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     };
 
     // S^T = K Q^T for the 64 keys of this tile (two 32-key blocks).
-    f32x16 sacc[PF_BN / 32];
+    f32x16 sacc[BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < PF_BN / 32; ++kb)
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
@@ -139,7 +141,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
         if (ks + KPF < KS) kread(ks + KPF);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -153,7 +155,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     float mx = kNegInf;
     if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -163,7 +165,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
             }
     } else {
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     }
@@ -186,7 +188,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     float lsum = 0.f;
     if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float sv = sacc[kb][r];
@@ -196,7 +198,7 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
             }
     } else {
 #pragma unroll
-        for (int kb = 0; kb < PF_BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
@@ -210,8 +212,8 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
     // O^T += V^T P^T, 16 keys per MFMA; the operands of the next key block
     // are read while the current one's MFMAs run.
 #pragma unroll
-    for (int c16 = 0; c16 < PF_BN / 16; ++c16) {
-        if (c16 + 1 < PF_BN / 16) vread(c16 + 1, va[(c16 + 1) & 1]);
+    for (int c16 = 0; c16 < BN / 16; ++c16) {
+        if (c16 + 1 < BN / 16) vread(c16 + 1, va[(c16 + 1) & 1]);
         const int kb = c16 >> 1, sh = (c16 & 1) * 8;
         bf16x8 pb;
 #pragma unroll

@@ -47,6 +47,31 @@ def check_dense_full(q, k, v, scale, causal, name=""):
     return eo, el
 
 
+def check_config_full(q, k, v, scale, causal, name=""):
+    """A full-size workload: the GPU output of the whole call compared with
+    the oracle at every element, one (batch, query head) at a time so the
+    host holds one head's float64 result at once.  Returns the worst o and
+    lse errors."""
+    announce(f"dense full {name} q={tuple(q.shape)} kv={tuple(k.shape)} {q.dtype} causal={causal}")
+    o, lse = run_fwd(q, k, v, scale, causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), name
+    B, Hq = q.shape[0], q.shape[1]
+    G = Hq // k.shape[1]
+    worst_o, worst_l = 0.0, 0.0
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            ro, rl = OA.attention(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, g:g + 1]), f64(v[b:b + 1, g:g + 1]),
+                                  scale, causal)
+            worst_o = max(worst_o, max_abs(f64(o[b:b + 1, h:h + 1]), ro))
+            worst_l = max(worst_l, max_abs(lse[b:b + 1, h:h + 1].double().numpy(), rl))
+    print(f"[parity] {name}: o max-abs {worst_o:.3e}, lse max-abs {worst_l:.3e}", file=sys.__stderr__,
+          flush=True)
+    assert worst_o <= O_TOL[q.dtype], f"{name}: o max-abs {worst_o}"
+    assert worst_l <= LSE_TOL, f"{name}: lse max-abs {worst_l}"
+    return worst_o, worst_l
+
+
 def check_dense_rows(o, lse, q, k, v, scale, causal, samples, name=""):
     """Sampled (b, h, rows) of a large run against the oracle, row by row."""
     worst_o, worst_l = 0.0, 0.0

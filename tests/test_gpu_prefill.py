@@ -13,7 +13,7 @@ import torch
 from exact_tiled_self_amd import AttnError, attn_fwd
 from exact_tiled_self_amd.inputs import DENSE_CONFIGS, dense_inputs
 from oracle import exact as OA
-from tests.gpu_util import (DEV, LSE_TOL, O_TOL, announce, check_dense_full, check_dense_rows,
+from tests.gpu_util import (DEV, LSE_TOL, O_TOL, announce, check_config_full, check_dense_full,
                             f64, max_abs, run_fwd)
 
 pytestmark = pytest.mark.gpu
@@ -51,23 +51,31 @@ def test_gqa_batches(dtype, B, Hq, Hkv, N, d, causal):
     check_dense_full(q, k, v, 1.0 / math.sqrt(d), causal, f"B{B}H{Hq}/{Hkv}N{N}")
 
 
+def fp32_o_tol(scale: float, d: int) -> float:
+    """The fp32 bound on o at any scale.  The stated 1e-5 is for the
+    workloads' scale 1/sqrt(d).  The kernel's fp32 dot product carries a
+    rounding error that the softmax sees multiplied by the scale, so at fixed
+    inputs the error of o grows in proportion to |scale|; the bound follows
+    it beyond 1/sqrt(d).  Measured on N(0,1) inputs (N = 150, both masks):
+    max error / (1e-5 |scale| sqrt(d)) stays between 0.05 and 0.1 for scales
+    -0.3 .. 2.5 and d = 64, 128, and is 0.03-0.05 of the bound at 1/sqrt(d)."""
+    return O_TOL[torch.float32] * max(1.0, abs(scale) * math.sqrt(d))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0, 2.5])
 def test_unusual_scales(dtype, d, scale):
-    """Scales far from 1/sqrt(d).  For fp32 the 1e-5 bound of the 1/sqrt(64)
-    workload is scaled by |scale| / 0.125 and by sqrt(d / 64): an fp32 dot
-    product carries a rounding error of order sqrt(d) * 2^-24 * |q||k|, and the
-    softmax weights see it multiplied by the scale."""
+    """Scales far from 1/sqrt(d).  bf16: the fixed 2e-2; fp32: the bound of
+    fp32_o_tol; lse: the fixed 1e-4 for both dtypes (measured <= 2.1e-5 up to
+    scale 2.5)."""
     q, k, v = dense_inputs(B=1, Hq=2, Hkv=2, N=150, d=d, dtype=dtype, seed=31)
-    tol = O_TOL[DT[dtype]]
-    if dtype == "f32":
-        tol *= max(1.0, abs(scale) / 0.125) * math.sqrt(d / 64)
+    tol = O_TOL[DT[dtype]] if dtype == "bf16" else fp32_o_tol(scale, d)
     for causal in (False, True):
         o, lse = run_fwd(q, k, v, scale, causal)
         ro, rl = OA.attention(f64(q), f64(k), f64(v), scale, causal)
         assert max_abs(f64(o), ro) <= tol
-        assert max_abs(lse.double().numpy(), rl) <= LSE_TOL * max(1.0, abs(scale) / 0.125)
+        assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
 
 
 # ------------------------------------------------- the pages' example ----
@@ -268,6 +276,31 @@ def test_pipelined_matches_plain(monkeypatch, B, Hq, Hkv, N):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 12, 2, 1000), (2, 4, 4, 333), (1, 2, 1, 31), (8, 2, 1, 300)])
+def test_second_tile_config(monkeypatch, d, causal, B, Hq, Hkv, N):
+    """Block-size invariance on the GPU: the key tiles may have any size
+    ("FlashAttention" notes: changing the block size changes no result).
+    The default launch (64-key tiles) and the plain kernel with 32-key tiles
+    (ATTN_PREFILL_BN=32) partition the keys differently, so the running
+    maximum is raised at different points; both must match the oracle and
+    each other within the tolerance, and each must be deterministic."""
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=500 + N + d)
+    scale = 1.0 / math.sqrt(d)
+    o1, l1 = run_fwd(q, k, v, scale, causal)
+    monkeypatch.setenv("ATTN_PREFILL_BN", "32")
+    o2, l2 = run_fwd(q, k, v, scale, causal)
+    o3, l3 = run_fwd(q, k, v, scale, causal)
+    assert torch.equal(o2.view(torch.int16), o3.view(torch.int16)) and torch.equal(l2, l3)
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), scale, causal)
+    for o, lse in ((o1, l1), (o2, l2)):
+        assert max_abs(f64(o), ro) <= O_TOL[torch.bfloat16]
+        assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
+    assert max_abs(f64(o1), f64(o2)) <= O_TOL[torch.bfloat16]
+    assert max_abs(l1.double().numpy(), l2.double().numpy()) <= LSE_TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,Hq,Hkv,N", [(8, 2, 1, 300), (4, 6, 2, 129), (2, 8, 8, 64), (1, 16, 8, 200)])
 def test_xcd_runs_cover_every_tile(d, B, Hq, Hkv, N):
     """Non-causal launches with a multiple of 8 kv heads (over the batch) map
@@ -343,47 +376,14 @@ def test_config_vit_fp32_full():
     check_dense_full(*dense_inputs(cfg), cfg.scale, cfg.causal, cfg.name)
 
 
-def test_config_vit_bf16_batched():
-    cfg = DENSE_CONFIGS["vit_b16_bf16"]
-    q, k, v = dense_inputs(cfg)
-    announce(cfg.name)
-    o, lse = run_fwd(q, k, v, cfg.scale, cfg.causal)
-    for b in (0, 17, 63):
-        ro, rl = OA.attention(f64(q[b:b + 1]), f64(k[b:b + 1]), f64(v[b:b + 1]), cfg.scale, False)
-        assert max_abs(f64(o[b:b + 1]), ro) <= O_TOL[q.dtype]
-        assert max_abs(lse[b:b + 1].double().numpy(), rl) <= LSE_TOL
-
-
-def test_config_vit_bf16_n577():
-    cfg = DENSE_CONFIGS["vit_b16_bf16_n577"]
-    q, k, v = dense_inputs(cfg)
-    announce(cfg.name)
-    o, lse = run_fwd(q, k, v, cfg.scale, cfg.causal)
-    for b in (0, 40):
-        ro, rl = OA.attention(f64(q[b:b + 1]), f64(k[b:b + 1]), f64(v[b:b + 1]), cfg.scale, False)
-        assert max_abs(f64(o[b:b + 1]), ro) <= O_TOL[q.dtype]
-        assert max_abs(lse[b:b + 1].double().numpy(), rl) <= LSE_TOL
-
-
-def _row_samples(rng, B, Hq, N, per_head, heads=None):
-    fixed = [0, 1, 63, 64, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1]
-    out = []
-    for h in (range(Hq) if heads is None else heads):
-        rows = fixed + list(rng.integers(0, N, per_head))
-        out.append((int(rng.integers(0, B)), h, [r for r in rows if 0 <= r < N]))
-    return out
-
-
-@pytest.mark.parametrize("name", ["gqa_causal_t8192", "mha_causal_t32768"])
-def test_config_long_causal_sampled(name):
+@pytest.mark.parametrize("name", ["vit_b16_bf16", "vit_b16_bf16_n577", "gqa_causal_t8192",
+                                  "mha_causal_t32768"])
+def test_config_full(name):
+    """Every output element of each full-size workload (64 images of 196 or
+    577 tokens; the 8192-token GQA and 32768-token MHA causal prefills)
+    against the oracle."""
     cfg = DENSE_CONFIGS[name]
-    q, k, v = dense_inputs(cfg)
-    announce(cfg.name)
-    o, lse = run_fwd(q, k, v, cfg.scale, True)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(123)
-    check_dense_rows(o, lse, f64(q), f64(k), f64(v), cfg.scale, True,
-                     _row_samples(rng, cfg.B, cfg.Hq, cfg.N, 24), cfg.name)
+    check_config_full(*dense_inputs(cfg), cfg.scale, cfg.causal, cfg.name)
 
 
 def test_long_prefill_allocates_nothing():
