@@ -6,7 +6,7 @@ the seeded input generators.  Importing the package does not load the
 library; the first call does, and raises if it is missing.
 """
 
-__all__ = ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+__all__ = ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size", "attn_paged_decode_noalloc",
            "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size",
            "attn_add_rmsnorm", "attn_swiglu",
            "AttnError", "library_path", "abi_version"]

@@ -19,6 +19,7 @@ import torch
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+           "attn_paged_decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES",
            "attn_kv_append", "attn_paged_prefill", "attn_bwd", "attn_bwd_workspace_size",
            "attn_add_rmsnorm", "attn_swiglu", "library_path", "abi_version", "raw_library", "ATTN_OK", "ATTN_ERR_INVALID_ARG",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_NO_DEVICE", "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_BF16"]
@@ -27,6 +28,10 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_NO_DEVICE, ATTN_ER
 ATTN_F32, ATTN_BF16 = 0, 1
 
 _DTYPE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+# ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h: the library's own
+# per-GPU array that attn_paged_decode_noalloc keeps its partial states in.
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -62,6 +67,9 @@ def raw_library():
         lib.attn_paged_decode.restype = ci
         lib.attn_paged_decode.argtypes = [vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci,
                                           cf, ci, vp, sz, vp]
+        lib.attn_paged_decode_noalloc.restype = ci
+        lib.attn_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci,
+                                                  cf, ci, vp]
         lib.attn_kv_append.restype = ci
         lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
                                        ci, vp]
@@ -209,6 +217,44 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, ctx_lens, block_size=16,
         _dev(o, "o"), _dev(lse, "lse") if lse is not None else None, S, Hq, Hkv, d, max_blocks,
         num_blocks, float(scale), _DTYPE[q.dtype], _dev(workspace, "workspace"), ws_bytes,
         _stream_ptr(q.device, stream))
+    _check(st)
+    return o, lse
+
+
+def attn_paged_decode_noalloc(q, k_cache, v_cache, block_table, ctx_lens, block_size=16, scale=None, *,
+                              o=None, lse=None, want_lse=True, stream=None):
+    """attn_paged_decode with no workspace: the partial states live in the
+    library's own per-GPU array (DECODE_NOALLOC_SCRATCH_BYTES), so with o
+    (and lse, or want_lse=False) passed in, the call allocates nothing.
+    Calls that may overlap on one GPU race on that array."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [S, Hq, d] and the caches [num_blocks, Hkv, block_size, d]")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise ValueError("block_table and ctx_lens must be int32")
+    if q.dtype not in _DTYPE or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype")
+    S, Hq, d = q.shape
+    num_blocks, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or bs != block_size or block_table.dim() != 2 or block_table.shape[0] != S \
+            or tuple(ctx_lens.shape) != (S,):
+        raise ValueError("inconsistent decode shapes")
+    max_blocks = block_table.shape[1]
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, ctx_lens=ctx_lens)
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _check_out(o, "o", (S, Hq, d), q.dtype, q)
+    if lse is None and want_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out(lse, "lse", (S, Hq), torch.float32, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = raw_library().attn_paged_decode_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(ctx_lens, "ctx_lens"), int(block_size),
+        _dev(o, "o"), _dev(lse, "lse") if lse is not None else None, S, Hq, Hkv, d, max_blocks,
+        num_blocks, float(scale), _DTYPE[q.dtype], _stream_ptr(q.device, stream))
     _check(st)
     return o, lse
 

@@ -138,12 +138,17 @@ size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, in
     return attn::decode_workspace_bound(S, Hq, d);
 }
 
-attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+}  // extern "C"
+
+namespace {
+
+static_assert(ATTN_DECODE_NOALLOC_SCRATCH_BYTES == attn::kDecodeScratchBytes, "scratch size");
+
+// Checks shared by both decode entry points (everything but the workspace).
+attn_status check_decode_args(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* ctx_lens, int block_size,
                               void* o, float* lse, int S, int Hq, int Hkv, int d, int max_blocks,
-                              int num_blocks, float scale, attn_dtype dtype, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-    g_err[0] = '\0';
+                              int num_blocks, float scale, attn_dtype dtype) {
     if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
         return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, ctx_lens and o must be non-null");
     if (S < 1 || Hq < 1 || Hkv < 1 || max_blocks < 1 || num_blocks < 1)
@@ -160,12 +165,8 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
         return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
     if ((long long)S * Hkv * max_blocks >= (1LL << 31) || S > 65535 || Hkv > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "too many sequences or blocks for one launch");
-    const size_t need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size);
-    if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-        !aligned(workspace, 16))
-        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and workspace must be 16-byte aligned");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
     if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || (lse && !aligned(lse, 4)))
         return fail(ATTN_ERR_INVALID_ARG, "block_table, ctx_lens and lse must be 4-byte aligned");
     const size_t es = 2;
@@ -174,15 +175,16 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
     const void* ins[5] = {q, k_cache, v_cache, block_table, ctx_lens};
     const size_t insz[5] = {qb, cb, cb, tb, lb};
     for (int i = 0; i < 5; ++i)
-        if (overlap(o, qb, ins[i], insz[i]) || overlap(lse, lsb, ins[i], insz[i]) ||
-            overlap(workspace, need, ins[i], insz[i]))
-            return fail(ATTN_ERR_INVALID_ARG, "outputs and workspace must not overlap the inputs");
-    if (overlap(o, qb, lse, lsb) || overlap(o, qb, workspace, need) || overlap(lse, lsb, workspace, need))
-        return fail(ATTN_ERR_INVALID_ARG, "o, lse and workspace must not overlap");
+        if (overlap(o, qb, ins[i], insz[i]) || overlap(lse, lsb, ins[i], insz[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "outputs must not overlap the inputs");
+    if (overlap(o, qb, lse, lsb)) return fail(ATTN_ERR_INVALID_ARG, "o and lse must not overlap");
+    return ATTN_OK;
+}
 
-    attn_status st = check_device();
-    if (st != ATTN_OK) return st;
-
+attn::DecodeArgs decode_args(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* ctx_lens, void* o, float* lse,
+                             int S, int Hq, int Hkv, int d, int max_blocks, int num_blocks, float scale,
+                             void* workspace) {
     attn::DecodeArgs a;
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table; a.ctx_lens = ctx_lens;
     a.o = o; a.lse = lse; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
@@ -190,7 +192,60 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
     a.c = (float)(fabs((double)scale) * 1.4426950408889634);
     a.negate = scale < 0.f ? 1 : 0;
     a.workspace = static_cast<float*>(workspace);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                              void* o, float* lse, int S, int Hq, int Hkv, int d, int max_blocks,
+                              int num_blocks, float scale, attn_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    attn_status st = check_decode_args(q, k_cache, v_cache, block_table, ctx_lens, block_size, o, lse, S, Hq,
+                                       Hkv, d, max_blocks, num_blocks, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_paged_decode_workspace_size(S, Hq, d, max_blocks, block_size);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const size_t es = 2;
+    const size_t qb = (size_t)S * Hq * d * es, cb = (size_t)num_blocks * Hkv * block_size * d * es;
+    const size_t tb = (size_t)S * max_blocks * 4, lb = (size_t)S * 4, lsb = lse ? (size_t)S * Hq * 4 : 0;
+    const void* others[7] = {q, k_cache, v_cache, block_table, ctx_lens, o, lse};
+    const size_t osz[7] = {qb, cb, cb, tb, lb, qb, lsb};
+    for (int i = 0; i < 7; ++i)
+        if (overlap(workspace, need, others[i], osz[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "the workspace must not overlap the inputs or outputs");
+
+    st = check_device();
+    if (st != ATTN_OK) return st;
+    const attn::DecodeArgs a = decode_args(q, k_cache, v_cache, block_table, ctx_lens, o, lse, S, Hq, Hkv, d,
+                                           max_blocks, num_blocks, scale, workspace);
     return launch_status(attn::launch_paged_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                                      void* o, float* lse, int S, int Hq, int Hkv, int d, int max_blocks,
+                                      int num_blocks, float scale, attn_dtype dtype, void* stream) {
+    g_err[0] = '\0';
+    attn_status st = check_decode_args(q, k_cache, v_cache, block_table, ctx_lens, block_size, o, lse, S, Hq,
+                                       Hkv, d, max_blocks, num_blocks, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn::decode_workspace_exact(S, Hq, Hkv, d);
+    if (need > attn::kDecodeScratchBytes)
+        return fail(ATTN_ERR_UNSUPPORTED, "this decode needs %zu bytes of partial states; the library's static "
+                    "scratch holds %zu (use attn_paged_decode with a workspace)", need, attn::kDecodeScratchBytes);
+
+    st = check_device();
+    if (st != ATTN_OK) return st;
+    const attn::DecodeArgs a = decode_args(q, k_cache, v_cache, block_table, ctx_lens, o, lse, S, Hq, Hkv, d,
+                                           max_blocks, num_blocks, scale, nullptr);
+    return launch_status(attn::launch_paged_decode_bf16_noalloc(a, static_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -43,6 +43,8 @@
 
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -467,6 +469,36 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     return a.d == 128 ? launch_decode_t<128>(a, stream) : launch_decode_t<64>(a, stream);
+}
+
+// The partial states of attn_paged_decode_noalloc: a device array owned by
+// the library, one copy per GPU (each device's code object holds its own),
+// alive until the process ends.  Host code never passes `scratch` itself to
+// a kernel (in host code the name stands for a host-side shadow): each
+// device's address is looked up once, with that device current, and kept.
+// Nothing in it has to start at zero: every slot a merge reads was written
+// by the same call's split kernel.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t launch_paged_decode_bf16_noalloc(DecodeArgs a, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    a.workspace = static_cast<float*>(ptr);
+    return launch_paged_decode_bf16(a, stream);
 }
 
 }  // namespace attn

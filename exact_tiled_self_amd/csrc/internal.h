@@ -68,6 +68,20 @@ struct DecodeArgs {
 
 hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Bytes of workspace a decode launch uses when Hkv is known (the size query
+// above bounds it over every Hkv instead).
+inline size_t decode_workspace_exact(int S, int Hq, int Hkv, int d) {
+    const int G = Hq / Hkv;
+    return decode_rec_bytes(S, Hkv) +
+           ((size_t)kDecodeWaves + (size_t)S * Hkv) * decode_slot_floats(G, d) * sizeof(float);
+}
+
+// The same decode with its partial states in the library's own per-device
+// scratch array (decode_paged.hip) instead of a caller workspace; the caller
+// has checked that decode_workspace_exact() fits kDecodeScratchBytes.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t launch_paged_decode_bf16_noalloc(DecodeArgs a, hipStream_t stream);
+
 // Packed new tokens [T, Hkv, d] written into the paged cache.
 struct KvAppendArgs {
     const void* k_new;

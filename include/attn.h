@@ -144,6 +144,35 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
                               void* stream);
 
 /*
+ * attn_paged_decode_noalloc - attn_paged_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, layouts, results and errors are those of attn_paged_decode
+ * (same kernels, bit-identical outputs), minus `workspace` and
+ * `workspace_bytes`.  The partial states that attn_paged_decode keeps in the
+ * caller's workspace live instead in a device array owned by the library,
+ * ATTN_DECODE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library
+ * runs on holds until the process ends.  A call whose partial states would
+ * not fit, i.e. when
+ *     256-byte-rounded(8 * S * Hkv)
+ *       + 4 * (2048 + S * Hkv) * (round4(2 * G) + G * d) > that size
+ * with G = Hq / Hkv, returns ATTN_ERR_UNSUPPORTED before anything is
+ * enqueued (S * Hkv up to about 8700 fits at G = 6, d = 128; about 1900 at
+ * G = 16).  Nothing is allocated, freed or memset.  Every call on one GPU
+ * shares that GPU's array, so calls that may run at the same time on one
+ * GPU (different streams, or host threads) race and must be ordered by the
+ * caller.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+attn_status attn_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      int block_size, void* o, float* lse, int S, int Hq, int Hkv,
+                                      int d, int max_blocks, int num_blocks, float scale,
+                                      attn_dtype dtype, void* stream);
+
+/*
  * attn_kv_append - write new tokens' keys and values into a paged KV cache
  * ("Kernels de atención rápida y fusión de operadores", section "Atención
  * tipo FlashAttention y atención paginada": the cache grows by a token, or a

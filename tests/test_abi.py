@@ -41,6 +41,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+                            "attn_paged_decode_noalloc",
                             "attn_kv_append", "attn_paged_prefill", "attn_bwd",
                             "attn_bwd_workspace_size", "attn_add_rmsnorm", "attn_swiglu",
                             "attn_status_string", "attn_last_error", "attn_abi_version"])
@@ -103,6 +104,43 @@ def dec(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A + 2
 def test_decode_rejects_before_any_launch(lib, kw, status):
     assert dec(lib, **kw) == status
     assert lib.attn_last_error().decode() != ""
+
+
+def dec_na(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A + 200 * MB, bs=16,
+           o=A + 208 * MB, lse=A + 216 * MB, S=4, Hq=12, Hkv=2, d=128, max_blocks=8, num_blocks=32,
+           scale=0.088, dtype=BF16):
+    return lib.attn_paged_decode_noalloc(q, kc, vc, table, ctx, bs, o, lse, S, Hq, Hkv, d, max_blocks,
+                                         num_blocks, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(kc=0), INVALID), (dict(table=0), INVALID), (dict(ctx=0), INVALID),
+    (dict(o=0), INVALID), (dict(S=0), INVALID), (dict(max_blocks=0), INVALID),
+    (dict(num_blocks=0), INVALID), (dict(Hq=12, Hkv=5), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(dtype=F32), UNSUPPORTED), (dict(d=80), UNSUPPORTED), (dict(bs=32), UNSUPPORTED),
+    (dict(q=A + 4), INVALID), (dict(table=A + 192 * MB + 2), INVALID), (dict(o=A + 64 * MB), INVALID),
+    (dict(lse=A + 208 * MB), INVALID),
+    # partial states of 2048 + S * Hkv pieces beyond the 32 MiB static array
+    (dict(S=9000, Hq=12, Hkv=2, max_blocks=1, o=A + 512 * MB, lse=A + 1024 * MB), UNSUPPORTED),
+    (dict(S=3000, Hq=16, Hkv=1, max_blocks=1, o=A + 512 * MB, lse=A + 1024 * MB), UNSUPPORTED),
+])
+def test_decode_noalloc_rejects_before_any_launch(lib, kw, status):
+    assert dec_na(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_decode_noalloc_capacity_bound():
+    """The documented fit rule against the header's constant: the full
+    64-sequence workload (12/2 heads, d = 128) fits, with room to spare."""
+    def need(S, Hq, Hkv, d):
+        G = Hq // Hkv
+        rec = (8 * S * Hkv + 255) // 256 * 256
+        return rec + 4 * (2048 + S * Hkv) * (((2 * G + 3) // 4 * 4) + G * d)
+    cap = _lib.DECODE_NOALLOC_SCRATCH_BYTES
+    assert need(64, 12, 2, 128) < cap // 4
+    assert need(4300, 12, 2, 128) <= cap < need(4400, 12, 2, 128)
+    assert need(1900, 16, 1, 128) <= cap < need(2000, 16, 1, 128)
+    assert need(9000, 12, 2, 128) > cap and need(3000, 16, 1, 128) > cap
 
 
 def test_workspace_size(lib):
@@ -245,6 +283,7 @@ def _gpu_present():
 def test_no_device_status(lib):
     assert fwd(lib) == NO_DEVICE
     assert dec(lib) == NO_DEVICE
+    assert dec_na(lib) == NO_DEVICE
     assert app(lib) == NO_DEVICE
     assert ppf(lib) == NO_DEVICE
     assert bwd(lib) == NO_DEVICE
