@@ -128,13 +128,36 @@ def profiled_traffic(profile: str, sources) -> float | None:
     return traffic if digest == h.hexdigest()[:16] else None
 
 
-def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100):
-    """The fp64 oracle, as it stands, on the prefill workload's host copy.
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
 
-    The whole workload fits in a few seconds of host time, so the sample is
-    the full forward pass, repeated until about `min_seconds` have elapsed.
+
+# Worker threads for the oracle: the host cores this process may use, capped
+# at 16, the CPU share a one-GPU machine gives a job (its affinity mask can show
+# the whole machine).
+CPU_WORKER_CAP = 16
+
+
+def cpu_workers(requested: int = 0) -> int:
+    return requested or min(CPU_WORKER_CAP, host_cores())
+
+
+def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100, heads=None):
+    """The fp64 oracle, as it stands, on a dense workload's host copy.
+
+    The sample is the whole forward pass, or the query heads `heads` of it
+    (every row of each: the oracle's cost per head is the same for all heads),
+    repeated until about `min_seconds` have elapsed; the rate is the sample's
+    algorithmic flops over its time.
     """
     from oracle import exact as OA
+    if heads is not None:
+        G = cfg.Hq // cfg.Hkv
+        kvh = sorted({h // G for h in heads})
+        q = q[:, list(heads)]
+        k, v = k[:, kvh], v[:, kvh]
+        if len(kvh) * G != len(heads):
+            raise ValueError("a head sample must be whole GQA groups")
     qn, kn, vn = (t.to("cpu").double().numpy() for t in (q, k, v))
     times = []
     while len(times) < max_reps and sum(times) < min_seconds:
@@ -142,10 +165,16 @@ def cpu_baseline(cfg, q, k, v, workers, min_seconds=10.0, max_reps=100):
         OA.attention(qn, kn, vn, cfg.scale, cfg.causal, workers=workers)
         times.append(time.perf_counter() - t0)
     dt = float(np.mean(times))
-    return {"value": round(prefill_flops(cfg) / dt / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": len(times),
-            "sample": f"the full {cfg.name} forward (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, "
-                      f"T={cfg.N}, d={cfg.d}, causal), float64 numpy oracle on the host copy"}
+    nh = cfg.Hq if heads is None else len(heads)
+    flops = prefill_flops(cfg) * nh / cfg.Hq
+    what = (f"the full {cfg.name} forward" if heads is None
+            else f"query heads {list(heads)} (all {cfg.N} rows each) of the {cfg.name} forward")
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
+            "host_cores": host_cores(), "worker_cap": CPU_WORKER_CAP,
+            "kind": "oracle", "seconds_per_pass": round(dt, 4), "passes": len(times),
+            "sample": f"{what} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, N={cfg.N}, d={cfg.d}, "
+                      f"{'causal' if cfg.causal else 'non-causal'}, {cfg.dtype}), float64 numpy oracle "
+                      f"on {workers} threads"}
 
 
 def plain_copy(torch, dev, mib):
@@ -159,12 +188,61 @@ def plain_copy(torch, dev, mib):
     del src, dst
 
 
-def run_configs(names, steps, warmup, copy_mib=0):
-    """attn_fwd alone on each named dense workload: HIP events on the launch
-    stream around every call; one JSON line per workload."""
-    import torch
+def dense_kernel_name(cfg) -> str:
+    if cfg.dtype == "f32":
+        return f"prefill_f32_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
+    if cfg.d == 128 and cfg.causal:
+        return f"prefill_sp_kernel<{cfg.d}, causal>"
+    return f"prefill_bf16_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
+
+
+def time_dense(torch, dev, stream, cfg, steps, warmup):
+    """attn_fwd alone on one dense workload, inputs resident: HIP events on
+    the launch stream around every call.  Returns the timing record."""
     from exact_tiled_self_amd import attn_fwd
-    from exact_tiled_self_amd.inputs import DENSE_CONFIGS, dense_inputs
+    from exact_tiled_self_amd.inputs import dense_inputs
+
+    q, k, v = (t.to(dev) for t in dense_inputs(cfg))
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device=dev)
+
+    def fwd():
+        attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, o=o, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        fwd()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for i in range(steps):
+        fwd()
+        e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[i].elapsed_time(e[i + 1]) for i in range(steps)]
+    del q, k, v, o, lse
+    avg_s = float(np.mean(ms)) / 1e3
+    fl, by = prefill_flops(cfg), prefill_bytes(cfg)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    tf, gb = fl / avg_s / 1e12, by / avg_s / 1e9
+    # the roof of this workload: its dtype's matrix peak, or the HBM peak times
+    # its arithmetic intensity when that is lower
+    roof = min(peak, fl / by * PEAK_HBM_GBPS / 1e3)
+    return {
+        "workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
+        "dtype": cfg.dtype, "causal": cfg.causal, "steps": steps, "warmup": warmup,
+        "avg_us": round(avg_s * 1e6, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+        "min_us": round(min(ms) * 1e3, 2),
+        "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / peak, 4), "mfma_peak_TFLOP/s": peak,
+        "GB/s": round(gb, 1), "frac_hbm": round(gb / PEAK_HBM_GBPS, 4),
+        "roof_TFLOP/s": round(roof, 1), "roof_bound": "mfma" if roof == peak else "hbm",
+        "frac_roof": round(tf / roof, 4),
+        "flops": fl, "algorithmic_bytes": int(by), "kernel": dense_kernel_name(cfg)}
+
+
+def run_configs(names, steps, warmup, copy_mib=0):
+    """attn_fwd alone on each named dense workload; one JSON line per workload."""
+    import torch
+    from exact_tiled_self_amd.inputs import DENSE_CONFIGS
 
     if names == ["all"]:
         names = list(DENSE_CONFIGS)
@@ -177,44 +255,75 @@ def run_configs(names, steps, warmup, copy_mib=0):
     if copy_mib > 0:
         plain_copy(torch, dev, copy_mib)
     for name in names:
-        cfg = DENSE_CONFIGS[name]
-        q, k, v = (t.to(dev) for t in dense_inputs(cfg))
-        o = torch.empty_like(q)
-        lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device=dev)
-
-        def fwd():
-            attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, o=o, lse=lse, stream=stream)
-
-        for _ in range(warmup):
-            fwd()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        torch.cuda.synchronize()
-        e[0].record(stream)
-        for i in range(steps):
-            fwd()
-            e[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms = [e[i].elapsed_time(e[i + 1]) for i in range(steps)]
-        avg_s = float(np.mean(ms)) / 1e3
-        fl, by = prefill_flops(cfg), prefill_bytes(cfg)
-        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-        if cfg.dtype == "f32":
-            kernel = f"prefill_f32_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
-        elif cfg.d == 128 and cfg.causal:
-            kernel = f"prefill_sp_kernel<{cfg.d}, causal>"
-        else:
-            kernel = f"prefill_bf16_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
-        print(json.dumps({
-            "workload": name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
-            "dtype": cfg.dtype, "causal": cfg.causal, "steps": steps, "warmup": warmup,
-            "avg_us": round(avg_s * 1e6, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
-            "min_us": round(min(ms) * 1e3, 2),
-            "TFLOP/s": round(fl / avg_s / 1e12, 2), "frac_mfma": round(fl / avg_s / 1e12 / peak, 4),
-            "mfma_peak_TFLOP/s": peak, "GB/s": round(by / avg_s / 1e9, 1),
-            "frac_hbm": round(by / avg_s / 1e9 / PEAK_HBM_GBPS, 4),
-            "flops": fl, "algorithmic_bytes": int(by), "kernel": kernel}), flush=True)
-        del q, k, v, o, lse
+        print(json.dumps(time_dense(torch, dev, stream, DENSE_CONFIGS[name], steps, warmup)), flush=True)
     return 0
+
+
+def profile_figures(profile: str, sources, kernel: str):
+    """Counter figures recorded in profiles/<profile>.md for one kernel:
+    HBM traffic per launch, MFMA busy fraction and the sustained shader clock
+    (GRBM_GUI_ACTIVE per XCD over the kernel-trace average), or None where
+    missing or taken on other sources than the current ones."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile + ".md")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        src = os.path.join(ROOT, "exact_tiled_self_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    text = open(path).read()
+    digest = None
+    for line in text.splitlines():
+        if line.startswith("source_sha256_16:"):
+            digest = line.split(":")[1].split()[0]
+    if digest != h.hexdigest()[:16]:
+        return None
+    vals, avg_ns = {}, None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0] == kernel and cells[1].isdigit():
+            avg_ns = float(cells[2])
+        elif len(cells) == 3 and cells[0] == kernel:
+            try:
+                vals[cells[1].split(" ")[0]] = float(cells[2])
+            except ValueError:
+                pass
+    out = {"traffic": profiled_traffic(profile, sources)}
+    if avg_ns and "GRBM_GUI_ACTIVE" in vals:
+        cyc = vals["GRBM_GUI_ACTIVE"] / 8.0           # per XCD
+        out["sclk_under_load_mhz"] = round(cyc / avg_ns * 1e3, 0)
+        out["trace_avg_us"] = round(avg_ns / 1e3, 2)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            out["mfma_busy"] = round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024), 4)
+    return out
+
+
+def consistency_checks(pre_prof, dec_prof, pre_flops, pre_seconds, dec_bytes):
+    """The measurement's own checks: the decode's counted HBM bytes must be
+    within 25 % of its algorithmic bytes (no re-reads, nothing skipped), and
+    the prefill's MFMA busy fraction must be at least what the event-timed
+    flops need at the clock the profile saw (a kernel cannot do its flops in
+    fewer matrix-core cycles than they take) and not far above it (wasted
+    matrix work).  A check whose counters are stale is reported as null."""
+    out = {}
+    tr = dec_prof.get("traffic") if dec_prof else None
+    out["decode_traffic_vs_algorithmic"] = (
+        {"ok": None, "why": "no profile of the current decode sources"} if tr is None else
+        {"ok": abs(tr / dec_bytes - 1.0) <= 0.25, "ratio": round(tr / dec_bytes, 4), "limit": 0.25})
+    if pre_prof and "mfma_busy" in pre_prof:
+        mhz = pre_prof["sclk_under_load_mhz"]
+        # bf16 32x32x16 MFMA: 1024 flops per cycle per SIMD, 1024 SIMDs
+        need = pre_flops / pre_seconds / (1024.0 * 1024.0 * mhz * 1e6)
+        busy = pre_prof["mfma_busy"]
+        out["prefill_mfma_busy_vs_events"] = {
+            "ok": 0.85 * need <= busy <= 1.6 * need, "mfma_busy": busy,
+            "needed_at_profiled_clock": round(need, 4), "sclk_mhz": mhz}
+    else:
+        out["prefill_mfma_busy_vs_events"] = {"ok": None, "why": "no profile of the current prefill sources"}
+    return out
 
 
 def read_clocks():
@@ -420,6 +529,13 @@ def main(argv=None):
     bq = OB.attention_bwd(qn[:, hs], kn, vn, dod[:, hs].double().cpu().numpy(), pcfg.scale, True)[0]
     berr = float(np.abs(dqd[:, hs].double().cpu().numpy() - bq).max() / max(1.0, np.abs(bq).max()))
 
+    # every dense workload alone (attn_fwd on resident inputs, events around
+    # each call): the ViT-B/16 shapes, the GQA prefill and the long MHA prefill
+    cfg_stats = {}
+    for name, cfg in DENSE_CONFIGS.items():
+        reps = K if cfg.N * cfg.N * cfg.B * cfg.Hq < 2e9 else max(10, K // 5)
+        cfg_stats[name] = time_dense(torch, dev, stream, cfg, reps, args.warmup)
+
     clocks = None if args.no_clocks else read_clocks()
 
     pf = prefill_flops(pcfg)
@@ -525,9 +641,35 @@ def main(argv=None):
         "clocks_after_timing": clocks,
         "library": _lib.library_path(),
     }
+    # counter figures of the committed profiles (null where the kernel
+    # sources changed since they were taken), and the consistency checks
+    # between them and the event timings
+    dec_prof = profile_figures("paged_decode_bf16_d128_s64", ["decode_paged.hip", "common.h", "internal.h"],
+                               "decode_split_kernel<128>")
+    pre_prof = profile_figures("prefill_bf16_d128_causal_gqa_t8192",
+                               ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"],
+                               "prefill_sp_kernel<128, true>")
+    out["roofline"]["profile"] = pre_prof
+    out["checks"] = consistency_checks(pre_prof, dec_prof, pf, pre_avg * 1e-3, db)
+    for name, ck in out["checks"].items():
+        if ck.get("ok") is False:
+            print(f"bench.py: CONSISTENCY CHECK FAILED: {name}: {ck}", file=sys.stderr, flush=True)
+    out["configs"] = cfg_stats
+
     if not args.no_cpu_baseline:
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        workers = cpu_workers(args.cpu_workers)
         out["cpu_baseline"] = cpu_baseline(pcfg, q, k, v, workers)
+        per = {}
+        for name, cfg in DENSE_CONFIGS.items():
+            if name == pcfg.name:
+                per[name] = out["cpu_baseline"]
+                continue
+            qc, kc, vc = dense_inputs(cfg)
+            # the 32768-token prefill: one GQA group of heads (one head) of it
+            heads = list(range(cfg.Hq // cfg.Hkv)) if cfg.N > 16384 else None
+            per[name] = cpu_baseline(cfg, qc, kc, vc, workers, min_seconds=2.0, heads=heads)
+            del qc, kc, vc
+        out["cpu_baseline_per_config"] = per
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
