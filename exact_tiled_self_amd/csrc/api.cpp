@@ -106,6 +106,9 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     // per-head byte offsets (plus one tile of look-ahead) must fit 32 bits
     if ((long long)N * d > (1LL << 31) - (1LL << 16))
         return fail(ATTN_ERR_UNSUPPORTED, "N * d must be at most 2^31 - 2^16");
+    // fp32: a head's bytes (4 per element) are addressed with 32-bit offsets
+    if (dtype == ATTN_F32 && (long long)N * d > (1LL << 29))
+        return fail(ATTN_ERR_UNSUPPORTED, "fp32: N * d must be at most 2^29");
     const int rows_per_wg = dtype == ATTN_F32 ? 16 : 64;   // the smallest row tile of either kernel
     const long long grid = (long long)B * Hq * ((N + rows_per_wg - 1) / rows_per_wg);
     if (grid >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -368,6 +371,9 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
     if ((long long)N * d > (1LL << 31) - (1LL << 16))
         return fail(ATTN_ERR_UNSUPPORTED, "N * d must be at most 2^31 - 2^16");
+    // fp32: a head's bytes (4 per element) are addressed with 32-bit offsets
+    if (dtype == ATTN_F32 && (long long)N * d > (1LL << 29))
+        return fail(ATTN_ERR_UNSUPPORTED, "fp32: N * d must be at most 2^29");
     const long long grid = (long long)B * Hq * ((N + 127) / 128);
     if (grid >= (1LL << 31) || (long long)B * Hq * N * (d / 8) >= (1LL << 38))
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");

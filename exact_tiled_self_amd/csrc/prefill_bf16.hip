@@ -195,6 +195,123 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
+// Short sequences at d = 64 (a ViT image: 196 tokens): one workgroup per
+// (b, head) holds the head's whole K and V in LDS, staged in one memory
+// round trip, and its 4 waves take the 32-row blocks of the head in turn
+// (wave w: blocks w, w + 4, ...), each walking the staged keys in 32-key
+// tiles with the same tile step as the tiled kernel.  SH_ROWS keys per head
+// at most: 52 KB of LDS, so three workgroups share a CU and a batch of
+// 64 images x 12 heads runs as a single round of workgroups.  The q tiles of
+// a head no longer each wait on their own key-tile loads, which is what
+// bounds the tiled kernel on such short rows.  Workgroups of heads that
+// share a kv head run back to back on one XCD (as in the non-causal tiled
+// kernel), so the shared K/V come from its L2.
+constexpr int SH_ROWS = 208;   // staged key rows (a multiple of 16)
+constexpr int SH_BN = 32;      // keys per tile step
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
+prefill_short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                     float* __restrict__ lse, int Hq, int Hkv, int N, int BH, float c, int negate) {
+    constexpr int D = 64;
+    constexpr int CPR = D / 8;
+    // K rows, then V rows: the K operand reads of a last 32-key tile that
+    // reach past the staged rows fall inside V (finite values, and those keys
+    // are masked); V rows past the staged ones are never read (VB = 1).
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SH_ROWS * D];
+    uint16_t* Ks = smem;
+    uint16_t* Vs = smem + SH_ROWS * D;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hi = lane >> 5, l32 = lane & 31;
+
+    // Workgroup w runs on XCD w % 8; the G heads that read one kv head are
+    // consecutive workgroups of one XCD.  Padding workgroups exit.
+    const int G = Hq / Hkv;
+    const int wg = blockIdx.x, x = wg & 7, j = wg >> 3;
+    const int r = (j / G) * 8 + x;
+    if (r >= BH / G) return;
+    const int bh = r * G + (j - (j / G) * G);
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / G;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+
+    // Stage rows 0 .. R-1 of K and V (R = N rounded up to 16; rows past N
+    // read as zero): 16-byte chunk p = i * 256 + tid is row p / CPR, chunk
+    // (p % CPR) ^ swizzle(row).  R * CPR is a multiple of 128, so the last
+    // round's guard is uniform per wave.
+    const int R = (N + 15) & ~15;
+    const int chunks = R * CPR;
+    for (int p0 = 0; p0 < chunks; p0 += PF_THREADS) {
+        if (p0 + wave * 64 < chunks) {
+            const int p = p0 + tid;
+            const int row = p / CPR;
+            const uint32_t ko = (uint32_t)(row * D + (((p % CPR) ^ kswz<CPR>(row)) * 8)) * 2;
+            const uint32_t vo = (uint32_t)(row * D + (((p % CPR) ^ vswz<CPR>(row)) * 8)) * 2;
+            buf_ld16_lds(krs, Ks + (p0 + wave * 64) * 8, ko);
+            buf_ld16_lds(vrs, Vs + (p0 + wave * 64) * 8, vo);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int n_rb = (N + 31) / 32;
+    for (int rb = wave; rb < n_rb; rb += PF_WAVES) {
+        const int wrow0 = rb * 32;
+        const int myrow = wrow0 + l32;
+        bf16x8 qf[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 w = buf_ld16(qrs, (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2);
+            if (negate) w = neg_bf16x8(w);
+            qf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+        f32x16 oacc[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+        float m_run = kNegInf, l_run = 0.f;
+
+        const int key_end = CAUSAL ? min(N, wrow0 + 32) : N;
+        const int n_kt = (key_end + SH_BN - 1) / SH_BN;
+        for (int kt = 0; kt < n_kt; ++kt) {
+            const int k0 = kt * SH_BN;
+            const bool need_mask = (k0 + SH_BN > N) || (CAUSAL && k0 + SH_BN - 1 > wrow0);
+            const uint16_t* Kt = Ks + k0 * D;
+            const uint16_t* Vt = Vs + k0 * D;
+            if (k0 + 16 >= R)     // only the tile's first 16 V rows are staged
+                pf_tile_step<D, CAUSAL, SH_BN, 1>(Kt, Vt, qf, oacc, m_run, l_run, k0, N, myrow, need_mask,
+                                                  c, hi, l32);
+            else
+                pf_tile_step<D, CAUSAL, SH_BN>(Kt, Vt, qf, oacc, m_run, l_run, k0, N, myrow, need_mask, c,
+                                               hi, l32);
+        }
+
+        // o = u / l, lse = m + ln l (natural log)
+        const float l_tot = l_run + xor_shfl(l_run, 32);
+        if (myrow < N) {
+            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+            uint16_t* orow = o + ((size_t)bh * N + myrow) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int dim0 = db * 32 + rg * 8 + hi * 4;
+                    const u32x2 w = {pack_bf16x2(oacc[db][rg * 4 + 0] * inv, oacc[db][rg * 4 + 1] * inv),
+                                     pack_bf16x2(oacc[db][rg * 4 + 2] * inv, oacc[db][rg * 4 + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + dim0) = w;
+                }
+            if (lse != nullptr && hi == 0) lse[(size_t)bh * N + myrow] = (m_run * c + log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
 // Software-pipelined variant: inside each wave, the vector work of key
 // tile j runs between the matrix instructions of its neighbours, because a
 // wave's own independent VALU instructions issue while its MFMAs execute
@@ -415,6 +532,18 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                                a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+            return hipGetLastError();
+        }
+    }
+    // Short d = 64 sequences over enough heads to fill the machine: one
+    // workgroup per head with the head's K and V staged whole.
+    if constexpr (D == 64) {
+        if (!bn32 && a.N <= SH_ROWS && BH >= 256) {
+            const long long padded = ((long long)BH / (a.Hq / a.Hkv) + 7) / 8 * 8 * (a.Hq / a.Hkv);
+            hipLaunchKernelGGL((prefill_short_kernel<CAUSAL>), dim3((unsigned)padded), block, 0, stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                               a.Hq, a.Hkv, a.N, BH, a.c, a.negate);
             return hipGetLastError();
         }
     }

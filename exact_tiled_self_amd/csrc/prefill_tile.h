@@ -84,7 +84,12 @@ constexpr float kLazyLog2 = 8.0f;
 // second tile configuration (any partition of the keys gives the same u / l).  Key position `key` is allowed for this lane's row iff
 // key < kend and (when CAUSAL) key <= mypos; `need_mask` must be true
 // whenever some key of the tile fails that test for some row of the wave.
-template <int D, bool CAUSAL, int BN = PF_BN>
+//
+// VB (default all) is the number of 16-key blocks of V the tile holds: a
+// last tile of 32 keys whose second 16 lie wholly past kend may be staged
+// with only its first 16 V rows (VB = 1); those keys are masked, so their
+// weights are 0 and their V rows are never read.
+template <int D, bool CAUSAL, int BN = PF_BN, int VB = BN / 16>
 __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t* Vs, const bf16x8* qf,
                                              f32x16* oacc, float& m_run, float& l_run, int k0,
                                              int kend, int mypos, bool need_mask, float c, int hi,
@@ -211,9 +216,10 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
 
     // O^T += V^T P^T, 16 keys per MFMA; the operands of the next key block
     // are read while the current one's MFMAs run.
+    static_assert(VB >= 1 && VB <= BN / 16, "V blocks");
 #pragma unroll
-    for (int c16 = 0; c16 < BN / 16; ++c16) {
-        if (c16 + 1 < BN / 16) vread(c16 + 1, va[(c16 + 1) & 1]);
+    for (int c16 = 0; c16 < VB; ++c16) {
+        if (c16 + 1 < VB) vread(c16 + 1, va[(c16 + 1) & 1]);
         const int kb = c16 >> 1, sh = (c16 & 1) * 8;
         bf16x8 pb;
 #pragma unroll

@@ -87,7 +87,7 @@ typedef enum {
  * o is written in `dtype` (round-to-nearest-even for bf16).
  *
  * Supported: dtype F32 or BF16; d = 64 or 128; B, Hq, Hkv, N >= 1;
- * N * d <= 2^31 - 2^16; q, k, v, o 16-byte aligned; lse 4-byte aligned.
+ * N * d <= 2^31 - 2^16 (2^29 for F32); q, k, v, o 16-byte aligned; lse 4-byte aligned.
  * Returns INVALID_ARG / UNSUPPORTED / NO_DEVICE / LAUNCH as described above.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

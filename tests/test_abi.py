@@ -76,7 +76,7 @@ def fwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * M
     (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
     (dict(q=A + 8), INVALID), (dict(o=A + 192 * MB + 4), INVALID), (dict(lse=A + 256 * MB + 2), INVALID),
     (dict(o=A), INVALID), (dict(lse=A + 64 * MB + 4096), INVALID), (dict(lse=A + 192 * MB), INVALID),
-    (dict(N=1 << 24, d=128), UNSUPPORTED),
+    (dict(N=1 << 24, d=128), UNSUPPORTED), (dict(N=(1 << 22) + 1, d=128, dtype=F32), UNSUPPORTED),
 ])
 def test_fwd_rejects_before_any_launch(lib, kw, status):
     assert fwd(lib, **kw) == status

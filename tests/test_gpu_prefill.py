@@ -41,6 +41,19 @@ def test_sweep_sizes(dtype, d, causal, N):
     check_dense_full(q, k, v, 1.0 / math.sqrt(d), causal, f"N={N}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(32, 8, 8, 1), (32, 8, 2, 15), (16, 16, 16, 16), (32, 8, 1, 17),
+                                        (64, 4, 4, 31), (32, 8, 4, 33), (32, 8, 8, 100), (64, 12, 12, 196),
+                                        (32, 8, 2, 207), (16, 16, 4, 208)])
+def test_short_sequences_whole_head_kernel(B, Hq, Hkv, N, causal):
+    """d = 64, N <= 208 over at least 256 heads: one workgroup per head with
+    the head's whole K and V staged in LDS (the batched ViT shape).  Every
+    element against the oracle, ragged N around the 16- and 32-key edges,
+    grouped and shared kv heads."""
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=64, dtype="bf16", seed=600 + N + Hq)
+    check_dense_full(q, k, v, 0.125, causal, f"short B{B}H{Hq}/{Hkv}N{N}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [
     (2, 6, 2, 300, 128, True), (2, 6, 3, 260, 64, False), (3, 4, 4, 129, 64, True),
