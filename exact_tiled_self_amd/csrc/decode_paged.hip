@@ -439,10 +439,10 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
 
 template <int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    // ATTN_DECODE_WAVES (4..2048, a multiple of 4) lowers the wave count so
+    // ATTN_DECODE_WAVES (4..2048, a multiple of 4) sets the wave count, so
     // that tests can reach long pieces, many pieces per wave and wide merges
     // with small inputs.
-    int waves = kDecodeWaves;
+    int waves = kDecodeWavesDefault;
     if (const char* env = getenv("ATTN_DECODE_WAVES")) {
         const int v = atoi(env);
         if (v >= 4 && v <= kDecodeWaves) waves = v / 4 * 4;

@@ -34,7 +34,12 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 // partial state (m, l, u) per query head in the workspace, which a second
 // kernel merges.
 constexpr int kDecodeBlock = 16;   // tokens per KV-cache block
-constexpr int kDecodeWaves = 2048; // waves of the split kernel (8 per CU on 256 CUs)
+constexpr int kDecodeWaves = 2048; // most waves a split kernel launch uses (sizes the workspace)
+// Waves launched by default: one 4-wave workgroup per CU of an MI355X.  Half
+// the maximum is faster (67.5 against 71.8 us for the 64-sequence workload,
+// cache flushed): each CU then runs a single workgroup, and a pair of
+// sequence and kv head is split into fewer pieces, so the merge is shorter.
+constexpr int kDecodeWavesDefault = 1024;
 
 // Workspace layout: per-pair records (first and last wave of the pair, two
 // int32 each) padded to 256 bytes, then one slot per (wave, pair) touch
