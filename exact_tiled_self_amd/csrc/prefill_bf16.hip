@@ -195,33 +195,149 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
-// Short sequences at d = 64 (a ViT image: 196 tokens): one workgroup per
-// (b, head) holds the head's whole K and V in LDS, staged in one memory
-// round trip, and its 4 waves take the 32-row blocks of the head in turn
-// (wave w: blocks w, w + 4, ...), each walking the staged keys in 32-key
-// tiles with the same tile step as the tiled kernel.  SH_ROWS keys per head
-// at most: 52 KB of LDS, so three workgroups share a CU and a batch of
-// 64 images x 12 heads runs as a single round of workgroups.  The q tiles of
-// a head no longer each wait on their own key-tile loads, which is what
-// bounds the tiled kernel on such short rows.  Workgroups of heads that
-// share a kv head run back to back on one XCD (as in the non-causal tiled
-// kernel), so the shared K/V come from its L2.
-constexpr int SH_ROWS = 208;   // staged key rows (a multiple of 16)
-constexpr int SH_BN = 32;      // keys per tile step
+// One step of the short-sequence kernel: a wave's 32 query rows against the
+// NBLK 32-key blocks of keys GK0 .. GK0 + 32 NBLK - 1, staged from row 0 of
+// Ks / Vs (d = 64), with the same online-softmax recurrence and MFMA layout
+// as pf_tile_step but up to 64 keys per step and every LDS read a per-lane
+// base plus an immediate.  Key `key` is allowed iff key < kend and (when
+// CAUSAL) key <= mypos; need_mask must be true when some key of the step
+// fails that for some row of the wave.  Only the first nvb 16-key blocks of
+// V are staged (the rest lie past kend: weights 0, never read).
+template <bool CAUSAL, int GK0, int NBLK>
+__device__ __forceinline__ void sh_step(const uint16_t* Ks, const uint16_t* Vs, const int (&kofs)[4],
+                                        const int (&vofs)[2], const bf16x8 (&qf)[4], f32x16 (&oacc)[2],
+                                        float& m_run, float& l_run, int kend, int mypos, bool need_mask, int nvb,
+                                        float c, int hi) {
+    constexpr int D = 64;
+    f32x16 sacc[NBLK];
+#pragma unroll
+    for (int kb = 0; kb < NBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    // S^T = K Q^T, block by block (K operands one MFMA ahead)
+    bf16x8 ka[2];
+    auto kread = [&](int i) {   // i = kb * 4 + ks
+        return *reinterpret_cast<const bf16x8*>(Ks + kofs[i & 3] + (i >> 2) * 32 * D);
+    };
+    ka[0] = kread(0);
+#pragma unroll
+    for (int i = 0; i < NBLK * 4; ++i) {
+        if (i + 1 < NBLK * 4) ka[(i + 1) & 1] = kread(i + 1);
+        sacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i & 1], qf[i & 3], sacc[i >> 2], 0, 0, 0);
+    }
 
-template <bool CAUSAL>
+    // row maximum (lane key of entry r in block kb: GK0 + 32 kb + 8 (r / 4) + 4 hi + r % 4)
+    float mx = kNegInf;
+    if (need_mask) {
+        // allowed iff 32 kb + 8 (r / 4) + r % 4 <= lim; lim passes through an
+        // empty asm so the compiler does not hoist the per-entry compares of
+        // every step out of the row loop (they would fill the scalar
+        // registers and spill)
+        int lim = kend - 1 - (GK0 + 4 * hi);
+        if (CAUSAL) lim = min(lim, mypos - (GK0 + 4 * hi));
+        asm("" : "+v"(lim));
+#pragma unroll
+        for (int kb = 0; kb < NBLK; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool ok = kb * 32 + 8 * (r >> 2) + (r & 3) <= lim;
+                sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+                mx = fmaxf(mx, sacc[kb][r]);
+            }
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < NBLK; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    }
+    mx = max_halves(mx);
+
+    // lazy rescale, as in pf_tile_step
+    const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+    }
+    const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+
+    // P = 2^(c s - c m) in bf16, row sum, and O^T += V^T P^T per 16 keys
+    float lsum = 0.f;
+    bf16x8 va[2][2];
+    auto vread = [&](int c16, bf16x8* dst) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const uint16_t* base = Vs + vofs[db] + c16 * 16 * D;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * D));
+            dst[db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    vread(0, va[0]);
+#pragma unroll
+    for (int c16 = 0; c16 < 2 * NBLK; ++c16) {
+        const int kb = c16 >> 1, sh = (c16 & 1) * 8;
+        bf16x8 pb;
+        if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float sv = sacc[kb][sh + i];
+                const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+                lsum += p;
+                pb[i] = (__bf16)p;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = fast_exp2(fmaf(sacc[kb][sh + i], c, -mc));
+                lsum += p;
+                pb[i] = (__bf16)p;
+            }
+        }
+        if (c16 < nvb) {
+            if (c16 + 1 < 2 * NBLK && c16 + 1 < nvb) vread(c16 + 1, va[(c16 + 1) & 1]);
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c16 & 1][db], pb, oacc[db], 0, 0, 0);
+        }
+    }
+    l_run += lsum;
+}
+
+// Short sequences at d = 64 (a ViT image: 196 tokens): one workgroup per
+// (b, head) holds the head's whole K and V in LDS, and its 4 waves take the
+// 32-row blocks of the head in turn (wave w: blocks w, w + 4, ...), each
+// walking the staged keys in steps of 64 (sh_step).  At most SH_ROWS = 208
+// keys: 52 KB of LDS, so three workgroups share a CU and a batch of 64
+// images x 12 heads runs as a single round of workgroups.  The keys are
+// staged in four parts (rows 0-63, 64-127, 128-191, 192-207), each in LDS
+// arrays of its own, and a wave's first row block computes a step as soon as
+// its part has landed (counted waits), so the loads of the later parts
+// overlap the first steps.  Heads that share a kv head run back to back on
+// one XCD (as in the non-causal tiled kernel), so the shared K/V come from
+// its L2.
+constexpr int SH_ROWS = 208;   // staged key rows: 3 parts of 64 and one of 16
+
+template <bool CAUSAL, bool PIPE>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 prefill_short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                      float* __restrict__ lse, int Hq, int Hkv, int N, int BH, float c, int negate) {
     constexpr int D = 64;
     constexpr int CPR = D / 8;
-    // K rows, then V rows: the K operand reads of a last 32-key tile that
-    // reach past the staged rows fall inside V (finite values, and those keys
-    // are masked); V rows past the staged ones are never read (VB = 1).
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SH_ROWS * D];
-    uint16_t* Ks = smem;
-    uint16_t* Vs = smem + SH_ROWS * D;
+    constexpr int PR = 64;                    // rows of a full part
+    // parts 0..2 (64 rows each) and part 3 (16 rows), each an array of its
+    // own (K rows, then V rows), so every read names the array it reads and
+    // the compiler does not wait for the loads still landing in the others
+    __shared__ __attribute__((aligned(16))) uint16_t P0s[2 * PR * D], P1s[2 * PR * D], P2s[2 * PR * D];
+    __shared__ __attribute__((aligned(16))) uint16_t P3s[2 * 16 * D];
+    uint16_t *K0s = P0s, *V0s = P0s + PR * D, *K1s = P1s, *V1s = P1s + PR * D;
+    uint16_t *K2s = P2s, *V2s = P2s + PR * D, *K3s = P3s, *V3s = P3s + 16 * D;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -241,61 +357,170 @@ prefill_short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
 
-    // Stage rows 0 .. R-1 of K and V (R = N rounded up to 16; rows past N
-    // read as zero): 16-byte chunk p = i * 256 + tid is row p / CPR, chunk
-    // (p % CPR) ^ swizzle(row).  R * CPR is a multiple of 128, so the last
-    // round's guard is uniform per wave.
-    const int R = (N + 15) & ~15;
-    const int chunks = R * CPR;
-    for (int p0 = 0; p0 < chunks; p0 += PF_THREADS) {
-        if (p0 + wave * 64 < chunks) {
-            const int p = p0 + tid;
-            const int row = p / CPR;
-            const uint32_t ko = (uint32_t)(row * D + (((p % CPR) ^ kswz<CPR>(row)) * 8)) * 2;
-            const uint32_t vo = (uint32_t)(row * D + (((p % CPR) ^ vswz<CPR>(row)) * 8)) * 2;
-            buf_ld16_lds(krs, Ks + (p0 + wave * 64) * 8, ko);
-            buf_ld16_lds(vrs, Vs + (p0 + wave * 64) * 8, vo);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+    // q rows of a row block: raw loads, then the sign (negative scale) once
+    // the loads are needed, so the first row block's loads stay in flight
+    // while the K/V parts are issued
+    auto load_q_raw = [&](int myrow, u32x4 (&qw)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qw[ks] = buf_ld16(qrs, (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2);
+    };
+    auto finish_q = [&](const u32x4 (&qw)[4], bf16x8 (&qf)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, negate ? neg_bf16x8(qw[ks]) : qw[ks]);
+    };
     const int n_rb = (N + 31) / 32;
-    for (int rb = wave; rb < n_rb; rb += PF_WAVES) {
+    bf16x8 qf[4];
+    u32x4 qw[4];
+
+    // Stage part p (rows 64p .. 64p + rows - 1 of K and V; rows past N read
+    // as zero): 16-byte chunk i * 256 + tid of the part is its row
+    // (i * 256 + tid) / 8, chunk ((i * 256 + tid) % 8) ^ swizzle(row).  A full
+    // part is exactly 2 chunks of K and 2 of V per thread (no guard, so the
+    // compiler counts them); a partial one guards whole waves.
+    const int R = (N + 15) & ~15;             // staged rows
+    auto stage_full = [&](int part, uint16_t* Kd, uint16_t* Vd) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pc = i * PF_THREADS + tid;
+            const int row = pc / CPR;
+            const int grow = part * PR + row;
+            buf_ld16_lds(krs, Kd + (i * PF_THREADS + wave * 64) * 8,
+                         (uint32_t)(grow * D + (((pc % CPR) ^ kswz<CPR>(row)) * 8)) * 2);
+            buf_ld16_lds(vrs, Vd + (i * PF_THREADS + wave * 64) * 8,
+                         (uint32_t)(grow * D + (((pc % CPR) ^ vswz<CPR>(row)) * 8)) * 2);
+        }
+    };
+    auto stage_part = [&](int part, uint16_t* Kd, uint16_t* Vd, int rows) {
+        const int chunks = rows * CPR;
+        for (int p0 = 0; p0 < chunks; p0 += PF_THREADS) {
+            if (p0 + wave * 64 < chunks) {
+                const int pc = p0 + tid;
+                const int row = pc / CPR;
+                const int grow = part * PR + row;
+                buf_ld16_lds(krs, Kd + (p0 + wave * 64) * 8,
+                             (uint32_t)(grow * D + (((pc % CPR) ^ kswz<CPR>(row)) * 8)) * 2);
+                buf_ld16_lds(vrs, Vd + (p0 + wave * 64) * 8,
+                             (uint32_t)(grow * D + (((pc % CPR) ^ vswz<CPR>(row)) * 8)) * 2);
+            }
+        }
+    };
+    const int rows0 = min(PR, R), rows1 = min(PR, max(0, R - PR)), rows2 = min(PR, max(0, R - 2 * PR));
+    const int rows3 = max(0, R - 3 * PR);
+    // PIPE (193 <= N <= 208: parts 0-2 full, part 3 sixteen rows): the
+    // 16-row part first, then parts 0, 1, 2, so that before step j < 3 the
+    // loads this thread may still have in flight are the 4 of each full part
+    // after j.  Otherwise every part is staged and waited for at once.
+    // (The first row block's q loads go between the 16-row part and part 0:
+    // the compiler counts the 12 part loads after them exactly, so its wait
+    // for q leaves parts 0-2 in flight.)
+    if (PIPE) {
+        stage_full(0, K0s, V0s);
+        // part 3 (16 rows, 128 chunks): waves 2 and 3 load the same chunks as
+        // waves 0 and 1 into the same places (identical bytes), so every
+        // thread issues exactly one K and one V load and nothing is guarded
+        {
+            const int pc = tid & 127;
+            const int row = pc / CPR;
+            const int grow = 3 * PR + row;
+            buf_ld16_lds(krs, K3s + ((wave & 1) * 64) * 8,
+                         (uint32_t)(grow * D + (((pc % CPR) ^ kswz<CPR>(row)) * 8)) * 2);
+            buf_ld16_lds(vrs, V3s + ((wave & 1) * 64) * 8,
+                         (uint32_t)(grow * D + (((pc % CPR) ^ vswz<CPR>(row)) * 8)) * 2);
+        }
+        load_q_raw(wave * 32 + l32, qw);
+        stage_full(1, K1s, V1s);
+        stage_full(2, K2s, V2s);
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        load_q_raw(wave * 32 + l32, qw);
+        stage_part(0, K0s, V0s, rows0);
+        stage_part(1, K1s, V1s, rows1);
+        stage_part(2, K2s, V2s, rows2);
+        stage_part(3, K3s, V3s, rows3);
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+    finish_q(qw, qf);
+    auto part_ready = [&](auto jp_tag) {   // every thread's loads of part jp have landed
+        constexpr int JP = decltype(jp_tag)::value;
+        // issued: part 0 (4 loads per thread), part 3 (2), q (4), parts 1, 2.
+        // A plain barrier: each thread has waited for its own loads of the
+        // part, and the barrier orders that before every wave's reads (a
+        // fenced barrier would drain every load still in flight).
+        if constexpr (JP == 0) {
+            wait_vmcnt<14>();
+            __builtin_amdgcn_s_barrier();
+        } else if constexpr (JP < 3) {
+            wait_vmcnt<4 * (2 - JP)>();
+            __builtin_amdgcn_s_barrier();
+        }
+    };
+
+    // per-lane LDS read offsets (elements): K operand of k-step ks (row l32 of
+    // a 32-key block; part 3 holds 16 rows, so its lanes 16..31 read row
+    // l32 - 16 instead: those keys lie past N and are masked), and the two
+    // V^T transpose reads per dims block; each one opaque, so every read stays
+    // a base plus an immediate
+    int kofs[4], kofs3[4], vofs[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        int off = l32 * D + (((ks * 2 + hi) ^ kswz<CPR>(l32)) * 8);
+        asm("" : "+v"(off));
+        kofs[ks] = off;
+        const int r3 = l32 & 15;
+        int off3 = r3 * D + (((ks * 2 + hi) ^ kswz<CPR>(r3)) * 8);
+        asm("" : "+v"(off3));
+        kofs3[ks] = off3;
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        int off = pf_vtr_offset<D>(lane, db);
+        asm("" : "+v"(off));
+        vofs[db] = off;
+    }
+
+    // One row block.  The first (row block `wave`, taken by every wave,
+    // with or without rows) passes the part barriers, which are
+    // workgroup-wide; its q rows were loaded before the parts.  It is a
+    // separate instantiation, so the compiler's waits for a later block's q
+    // rows do not tighten the part waits.
+    auto row_block = [&](auto first_tag, int rb) {
+        constexpr bool FIRST = decltype(first_tag)::value;
         const int wrow0 = rb * 32;
         const int myrow = wrow0 + l32;
-        bf16x8 qf[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 w = buf_ld16(qrs, (uint32_t)(myrow * D + ks * 16 + hi * 8) * 2);
-            if (negate) w = neg_bf16x8(w);
-            qf[ks] = __builtin_bit_cast(bf16x8, w);
+        const bool active = rb < n_rb;
+        if (!FIRST) {
+            load_q_raw(myrow, qw);
+            finish_q(qw, qf);
         }
-        f32x16 oacc[D / 32];
+        f32x16 oacc[2];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
         float m_run = kNegInf, l_run = 0.f;
 
+        // steps of 64 keys over parts 0..2, then the 16 keys of part 3
         const int key_end = CAUSAL ? min(N, wrow0 + 32) : N;
-        const int n_kt = (key_end + SH_BN - 1) / SH_BN;
-        for (int kt = 0; kt < n_kt; ++kt) {
-            const int k0 = kt * SH_BN;
-            const bool need_mask = (k0 + SH_BN > N) || (CAUSAL && k0 + SH_BN - 1 > wrow0);
-            const uint16_t* Kt = Ks + k0 * D;
-            const uint16_t* Vt = Vs + k0 * D;
-            if (k0 + 16 >= R)     // only the tile's first 16 V rows are staged
-                pf_tile_step<D, CAUSAL, SH_BN, 1>(Kt, Vt, qf, oacc, m_run, l_run, k0, N, myrow, need_mask,
-                                                  c, hi, l32);
-            else
-                pf_tile_step<D, CAUSAL, SH_BN>(Kt, Vt, qf, oacc, m_run, l_run, k0, N, myrow, need_mask, c,
-                                               hi, l32);
-        }
+        auto step = [&](auto gk0_tag, auto nblk_tag, const uint16_t* Kp, const uint16_t* Vp, const int (&ko)[4],
+                        int part_rows) {
+            constexpr int GK0 = decltype(gk0_tag)::value, NB = decltype(nblk_tag)::value;
+            if (PIPE && FIRST) part_ready(std::integral_constant<int, GK0 / PR>{});
+            if (active && GK0 < key_end) {
+                const bool need_mask = (GK0 + 32 * NB > N) || (CAUSAL && GK0 + 32 * NB - 1 > wrow0);
+                sh_step<CAUSAL, GK0, NB>(Kp, Vp, ko, vofs, qf, oacc, m_run, l_run, N, myrow, need_mask,
+                                         min(2 * NB, part_rows / 16), c, hi);
+            }
+        };
+        using std::integral_constant;
+        step(integral_constant<int, 0>{}, integral_constant<int, 2>{}, K0s, V0s, kofs, rows0);
+        step(integral_constant<int, 64>{}, integral_constant<int, 2>{}, K1s, V1s, kofs, rows1);
+        step(integral_constant<int, 128>{}, integral_constant<int, 2>{}, K2s, V2s, kofs, rows2);
+        step(integral_constant<int, 192>{}, integral_constant<int, 1>{}, K3s, V3s, kofs3, rows3);
 
         // o = u / l, lse = m + ln l (natural log)
         const float l_tot = l_run + xor_shfl(l_run, 32);
-        if (myrow < N) {
+        if (active && myrow < N) {
             const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
             uint16_t* orow = o + ((size_t)bh * N + myrow) * D;
 #pragma unroll
@@ -309,7 +534,9 @@ prefill_short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 }
             if (lse != nullptr && hi == 0) lse[(size_t)bh * N + myrow] = (m_run * c + log2f(l_tot)) * kLn2;
         }
-    }
+    };
+    row_block(std::true_type{}, wave);
+    for (int rb = wave + PF_WAVES; rb < n_rb; rb += PF_WAVES) row_block(std::false_type{}, rb);
 }
 
 // Software-pipelined variant: inside each wave, the vector work of key
@@ -540,10 +767,16 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     if constexpr (D == 64) {
         if (!bn32 && a.N <= SH_ROWS && BH >= 256) {
             const long long padded = ((long long)BH / (a.Hq / a.Hkv) + 7) / 8 * 8 * (a.Hq / a.Hkv);
-            hipLaunchKernelGGL((prefill_short_kernel<CAUSAL>), dim3((unsigned)padded), block, 0, stream,
-                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                               a.Hq, a.Hkv, a.N, BH, a.c, a.negate);
+            if (a.N > 3 * 64 && a.N <= SH_ROWS)
+                hipLaunchKernelGGL((prefill_short_kernel<CAUSAL, true>), dim3((unsigned)padded), block, 0, stream,
+                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                                   static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                                   a.Hq, a.Hkv, a.N, BH, a.c, a.negate);
+            else
+                hipLaunchKernelGGL((prefill_short_kernel<CAUSAL, false>), dim3((unsigned)padded), block, 0, stream,
+                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                                   static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                                   a.Hq, a.Hkv, a.N, BH, a.c, a.negate);
             return hipGetLastError();
         }
     }
