@@ -8,8 +8,9 @@
 // e^(m - m').  Only O = u / l and lse = m + ln l are written.  Scores are
 // handled in base 2 with c = scale * log2(e).
 //
-// fp32 throughout: FMA on the vector ALU, no reduced-precision step, so the
-// result stays within a few fp32 ulps of the exact one.
+// fp32 throughout: fp32 products and sums (fp32 matrix cores at d = 64, FMA
+// on the vector ALU at d = 128), no reduced-precision step, so the result
+// stays within a few fp32 ulps of the exact one.
 
 #include "common.h"
 #include "internal.h"
@@ -165,6 +166,192 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// ------------------------------------------------------- fp32 on MFMA ----
+// d = 64 on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32 operands,
+// fp32 accumulation; no reduced-precision step).  A workgroup owns one 32-row
+// query block of one head; its W waves (at most 8) take the head's 32-key
+// blocks in turn (wave w: blocks w, w + W, ...), each with its own running
+// (m, l, u) per row, and the W partial states of a row are merged through LDS
+// at the end with M = max m_w, L = sum l_w e^(m_w - M), U = sum u_w
+// e^(m_w - M), o = U / L.  The operands come straight from memory into
+// registers, so a key block costs one memory round trip and the matrix
+// cores, not LDS traffic:
+//   * S^T = K Q^T: lane l gives K[key l % 32][dim 32 (l / 32) + s] and
+//     Q[row l % 32][the same dim] at step s (the dims are split between the
+//     two lane halves, each half walking its 32 in order: 32 steps of 2);
+//     lane l gets back the scores of row l % 32 with keys
+//     8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15.
+//   * O^T += V^T P^T: step s pairs key 8 (s / 4) + 4 h + s % 4 with lane half
+//     h, which is exactly the lane's own score entry r = s, so P^T is the
+//     lane's weights in order and V^T is V[that key][dim 32 db + l % 32].
+constexpr int F32M_MAXW = 8;
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(64 * F32M_MAXW)
+prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+                        float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, int BH,
+                        int n_qb, float c, int negate) {
+    constexpr int D = 64;
+    // partial states: u[w][entry][lane] (lane fastest: no bank conflicts),
+    // then m and l per (w, row); the merged output tile, [32 rows][65] (one
+    // float of padding per row), reuses the u area
+    constexpr int OS = D + 1;
+    __shared__ __attribute__((aligned(16))) float su[F32M_MAXW * 32 * 64];
+    __shared__ float sm[F32M_MAXW * 32], sl[F32M_MAXW * 32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int W = blockDim.x >> 6;
+    const int h2 = lane >> 5, l32 = lane & 31;
+    const int wg = blockIdx.x;
+    const int qb = CAUSAL ? (n_qb - 1 - wg / BH) : (wg / BH);
+    const int bh = wg % BH;
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    const uint32_t head_bytes = (uint32_t)N * D * 4;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const int q0 = qb * 32;
+    const int myrow = q0 + l32;
+    const int n_kb = CAUSAL ? min(qb + 1, (N + 31) / 32) : (N + 31) / 32;
+
+    // q: row l32, dims 32 h2 .. 32 h2 + 31 (zero past N).  A negative scale
+    // negates the scores after the product instead of q, so nothing waits for
+    // these loads before the key blocks' loads are issued.
+    float qv[32];
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+        const f32x4 x = __builtin_bit_cast(f32x4, buf_ld16(qrs, (uint32_t)(myrow * D + 32 * h2 + i) * 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[i + j] = x[j];
+    }
+
+    f32x16 oacc[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    for (int kb = wave; kb < n_kb; kb += W) {
+        const int k0 = kb * 32;
+        // K row k0 + l32, dims 32 h2 ..; V rows of the pairing, dims 32 db + l32
+        float kv[32], vv[2][16];
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+            const f32x4 x = __builtin_bit_cast(f32x4, buf_ld16(krs, (uint32_t)((k0 + l32) * D + 32 * h2 + i) * 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kv[i + j] = x[j];
+        }
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const int key = k0 + 8 * (st >> 2) + 4 * h2 + (st & 3);
+                vv[db][st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                            vrs, (uint32_t)(key * D + 32 * db + l32) * 4, 0, 0));
+            }
+        // every load of the block is issued before the first product uses
+        // one (otherwise the compiler interleaves them with the products and
+        // each K load becomes its own round trip)
+        __builtin_amdgcn_sched_barrier(0);
+
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 32; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[st], qv[st], sacc, 0, 0, 0);
+        if (negate) sacc = -sacc;   // (-q).k, exactly
+
+        // mask, row maximum (the row's 32 keys: 16 in this lane, 16 in lane ^ 32)
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= myrow);
+            sacc[r] = ok ? sacc[r] : kNegInf;
+            mx = fmaxf(mx, sacc[r]);
+        }
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_use) * c);
+        float lsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = (sacc[r] == kNegInf) ? 0.f : fast_exp2((sacc[r] - m_use) * c);
+            sacc[r] = p;
+            lsum += p;
+        }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            oacc[db] *= alpha;
+#pragma unroll
+            for (int st = 0; st < 16; ++st)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[db][st], sacc[st], oacc[db], 0, 0, 0);
+        }
+        m_run = m_new;
+    }
+    // the row's sum over both lane halves
+    l_run += __shfl_xor(l_run, 32, 64);
+
+    // merge the W partial states of each row through LDS
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) su[(wave * 32 + db * 16 + r) * 64 + lane] = oacc[db][r];
+    if (h2 == 0) {
+        sm[wave * 32 + l32] = m_run;
+        sl[wave * 32 + l32] = l_run;
+    }
+    __syncthreads();
+    float M = kNegInf, L = 0.f;
+    float f[F32M_MAXW];
+    if (wave == 0) {
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm[w * 32 + l32]);
+#pragma unroll
+        for (int w = 0; w < F32M_MAXW; ++w) {
+            const float mw = w < W ? sm[w * 32 + l32] : kNegInf;
+            f[w] = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * c);
+            L = w < W ? fmaf(f[w], sl[w * 32 + l32], L) : L;
+        }
+    }
+    float res[32];
+    if (wave == 0) {
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float u = 0.f;
+#pragma unroll
+            for (int w = 0; w < F32M_MAXW; ++w)
+                if (w < W) u = fmaf(f[w], su[(w * 32 + i) * 64 + lane], u);
+            res[i] = u * inv;
+        }
+    }
+    __syncthreads();
+    // transpose through LDS into [row][dim] and store whole rows
+    float* so = su;   // [32 rows][OS]
+    if (wave == 0) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                so[l32 * OS + 32 * db + 8 * (r >> 2) + 4 * h2 + (r & 3)] = res[db * 16 + r];
+        if (lse != nullptr && h2 == 0 && myrow < N) lse[(size_t)bh * N + myrow] = (M * c + log2f(L)) * kLn2;
+    }
+    __syncthreads();
+    for (int e = tid * 4; e < 32 * D; e += blockDim.x * 4) {
+        const int row = e / D, col = e % D;
+        if (q0 + row < N) {
+            const float* src = &so[row * OS + col];
+            *reinterpret_cast<f32x4*>(o + ((size_t)bh * N + q0 + row) * D + col) =
+                f32x4{src[0], src[1], src[2], src[3]};
+        }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.Hq;
@@ -181,7 +368,21 @@ hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 128) return a.causal ? launch_f32_t<128, true>(a, stream) : launch_f32_t<128, false>(a, stream);
-    return a.causal ? launch_f32_t<64, true>(a, stream) : launch_f32_t<64, false>(a, stream);
+    // d = 64: the matrix-core kernel, one 32-row block per workgroup and at
+    // most 8 waves over the key blocks
+    const int BH = a.B * a.Hq;
+    const int n_qb = (a.N + 31) / 32;
+    const int W = min(F32M_MAXW, n_qb);
+    const dim3 grid((unsigned)(BH * n_qb)), block((unsigned)(64 * W));
+    if (a.causal)
+        hipLaunchKernelGGL((prefill_f32_mfma_kernel<true>), grid, block, 0, stream, static_cast<const float*>(a.q),
+                           static_cast<const float*>(a.k), static_cast<const float*>(a.v), static_cast<float*>(a.o),
+                           a.lse, a.Hq, a.Hkv, a.N, BH, n_qb, a.c, a.negate);
+    else
+        hipLaunchKernelGGL((prefill_f32_mfma_kernel<false>), grid, block, 0, stream, static_cast<const float*>(a.q),
+                           static_cast<const float*>(a.k), static_cast<const float*>(a.v), static_cast<float*>(a.o),
+                           a.lse, a.Hq, a.Hkv, a.N, BH, n_qb, a.c, a.negate);
+    return hipGetLastError();
 }
 
 }  // namespace attn
