@@ -357,6 +357,8 @@ def main(argv=None):
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing each dense workload alone (profiling runs of the bench kernels)")
     ap.add_argument("--configs", default=None,
                     help="comma-separated dense workloads (or 'all'): time attn_fwd alone on each "
                          "and print one JSON line per workload instead of the bench line")
@@ -537,7 +539,7 @@ def main(argv=None):
     # every dense workload alone (attn_fwd on resident inputs, events around
     # each call): the ViT-B/16 shapes, the GQA prefill and the long MHA prefill
     cfg_stats = {}
-    for name, cfg in DENSE_CONFIGS.items():
+    for name, cfg in ({} if args.no_configs else DENSE_CONFIGS).items():
         reps = K if cfg.N * cfg.N * cfg.B * cfg.Hq < 2e9 else max(10, K // 5)
         cfg_stats[name] = time_dense(torch, dev, stream, cfg, reps, args.warmup)
 
