@@ -299,8 +299,11 @@ def profile_figures(profile: str, sources, kernel: str):
     out = {"traffic": profiled_traffic(profile, sources)}
     if avg_ns and "GRBM_GUI_ACTIVE" in vals:
         cyc = vals["GRBM_GUI_ACTIVE"] / 8.0           # per XCD
-        out["sclk_under_load_mhz"] = round(cyc / avg_ns * 1e3, 0)
         out["trace_avg_us"] = round(avg_ns / 1e3, 2)
+        # GRBM_GUI_ACTIVE also counts the busy time around each dispatch, so
+        # cycles over the trace time only estimate the clock for long kernels
+        if avg_ns >= 1e5:
+            out["sclk_under_load_mhz"] = round(cyc / avg_ns * 1e3, 0)
         if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
             out["mfma_busy"] = round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024), 4)
     return out
