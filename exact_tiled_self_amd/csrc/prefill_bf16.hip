@@ -51,8 +51,18 @@
 namespace attn {
 namespace {
 
+// Waves per SIMD of prefill_bf16_kernel: 4 for d = 64 on 32-key tiles
+// (state in 128 registers: one wave alone issues vector instructions at
+// about half the SIMD's rate, so the softmax-heavy d = 64 loop gains from
+// more resident waves), 2 elsewhere (256 registers).
+template <int D, int BN>
+constexpr int pf_waves_per_eu() {
+    return (D == 64 && BN == 32) ? 4 : 2;
+}
+
 template <int D, bool CAUSAL, int BN>
-__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(PF_THREADS)
+    __attribute__((amdgpu_waves_per_eu(pf_waves_per_eu<D, BN>(), pf_waves_per_eu<D, BN>())))
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                     float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
@@ -745,16 +755,20 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // the non-causal d = 128 build of the pipelined loop runs out of registers.
     // Scale 0 also takes the plain kernel: the pipelined one relies on
     // 2^(c * -inf - c m) being 0 for masked keys, which needs c > 0.
-    // ATTN_PREFILL_BN=32 (test hook): the plain kernel with 32-key tiles, a
-    // second partition of the keys, which must give the same result within
-    // the tolerances.
+    // The plain kernel's key tiles: 64 keys at d = 128, 32 at d = 64 (four
+    // waves per SIMD).  ATTN_PREFILL_BN=32 or 64 (test hook) forces the plain
+    // kernel with that tile, another partition of the keys, which must give
+    // the same result within the tolerances.
     const char* bn_env = getenv("ATTN_PREFILL_BN");
-    const bool bn32 = bn_env != nullptr && bn_env[0] == '3' && bn_env[1] == '2' && bn_env[2] == '\0';
+    const bool force32 = bn_env != nullptr && bn_env[0] == '3' && bn_env[1] == '2' && bn_env[2] == '\0';
+    const bool force64 = bn_env != nullptr && bn_env[0] == '6' && bn_env[1] == '4' && bn_env[2] == '\0';
+    const bool bn_forced = force32 || force64;
+    const bool bn32 = force32 || (D == 64 && !force64);
     if constexpr (D == 128 && CAUSAL) {
         // ATTN_PREFILL_PLAIN=1 (test hook) keeps the plain kernel, so tests
         // can compare the two
         const char* plain = getenv("ATTN_PREFILL_PLAIN");
-        if (a.c > 0.f && !bn32 && !(plain != nullptr && plain[0] == '1')) {
+        if (a.c > 0.f && !bn_forced && !(plain != nullptr && plain[0] == '1')) {
             hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
@@ -765,7 +779,7 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // Short d = 64 sequences over enough heads to fill the machine: one
     // workgroup per head with the head's K and V staged whole.
     if constexpr (D == 64) {
-        if (!bn32 && a.N <= SH_ROWS && BH >= 256) {
+        if (!bn_forced && a.N <= SH_ROWS && BH >= 256) {
             const long long padded = ((long long)BH / (a.Hq / a.Hkv) + 7) / 8 * 8 * (a.Hq / a.Hkv);
             if (a.N > 3 * 64 && a.N <= SH_ROWS)
                 hipLaunchKernelGGL((prefill_short_kernel<CAUSAL, true>), dim3((unsigned)padded), block, 0, stream,

@@ -294,14 +294,15 @@ def test_pipelined_matches_plain(monkeypatch, B, Hq, Hkv, N):
 def test_second_tile_config(monkeypatch, d, causal, B, Hq, Hkv, N):
     """Block-size invariance on the GPU: the key tiles may have any size
     ("FlashAttention" notes: changing the block size changes no result).
-    The default launch (64-key tiles) and the plain kernel with 32-key tiles
-    (ATTN_PREFILL_BN=32) partition the keys differently, so the running
-    maximum is raised at different points; both must match the oracle and
-    each other within the tolerance, and each must be deterministic."""
+    The default launch (64-key tiles at d = 128, 32-key tiles at d = 64) and
+    the plain kernel forced to the other tile size (ATTN_PREFILL_BN)
+    partition the keys differently, so the running maximum is raised at
+    different points; both must match the oracle and each other within the
+    tolerance, and each must be deterministic."""
     q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=500 + N + d)
     scale = 1.0 / math.sqrt(d)
     o1, l1 = run_fwd(q, k, v, scale, causal)
-    monkeypatch.setenv("ATTN_PREFILL_BN", "32")
+    monkeypatch.setenv("ATTN_PREFILL_BN", "32" if d == 128 else "64")
     o2, l2 = run_fwd(q, k, v, scale, causal)
     o3, l3 = run_fwd(q, k, v, scale, causal)
     assert torch.equal(o2.view(torch.int16), o3.view(torch.int16)) and torch.equal(l2, l3)
