@@ -257,11 +257,17 @@ prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k
         // each K load becomes its own round trip)
         __builtin_amdgcn_sched_barrier(0);
 
-        f32x16 sacc;
+        // two accumulators (even and odd k-steps), so that consecutive
+        // products do not wait for each other's results
+        f32x16 sacc, sacc1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = sacc1[r] = 0.f;
 #pragma unroll
-        for (int st = 0; st < 32; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[st], qv[st], sacc, 0, 0, 0);
+        for (int st = 0; st < 32; st += 2) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[st], qv[st], sacc, 0, 0, 0);
+            sacc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[st + 1], qv[st + 1], sacc1, 0, 0, 0);
+        }
+        sacc += sacc1;
         if (negate) sacc = -sacc;   // (-q).k, exactly
 
         // mask, row maximum (the row's 32 keys: 16 in this lane, 16 in lane ^ 32)
@@ -285,13 +291,13 @@ prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k
             lsum += p;
         }
         l_run = l_run * alpha + lsum;
+        oacc[0] *= alpha;
+        oacc[1] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            oacc[db] *= alpha;
+        for (int st = 0; st < 16; ++st)
 #pragma unroll
-            for (int st = 0; st < 16; ++st)
+            for (int db = 0; db < 2; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[db][st], sacc[st], oacc[db], 0, 0, 0);
-        }
         m_run = m_new;
     }
     // the row's sum over both lane halves
@@ -307,40 +313,59 @@ prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k
         sl[wave * 32 + l32] = l_run;
     }
     __syncthreads();
+    // Every wave forms the weights e^(m_w - M) of the W states of its lanes'
+    // rows and merges the groups of 4 entries wave, wave + W, ... of the
+    // numerator (W-fold fewer LDS reads per wave than one wave merging all
+    // 32).
+    // (Branch-free: state w >= W reads state W - 1 with weight 0, so that
+    // all of a group's LDS reads issue together.)
     float M = kNegInf, L = 0.f;
-    float f[F32M_MAXW];
-    if (wave == 0) {
-        for (int w = 0; w < W; ++w) M = fmaxf(M, sm[w * 32 + l32]);
+    float f[F32M_MAXW], mw[F32M_MAXW], lw[F32M_MAXW];
 #pragma unroll
-        for (int w = 0; w < F32M_MAXW; ++w) {
-            const float mw = w < W ? sm[w * 32 + l32] : kNegInf;
-            f[w] = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * c);
-            L = w < W ? fmaf(f[w], sl[w * 32 + l32], L) : L;
-        }
+    for (int w = 0; w < F32M_MAXW; ++w) {
+        const int wc = min(w, W - 1);
+        mw[w] = sm[wc * 32 + l32];
+        lw[w] = sl[wc * 32 + l32];
+        M = fmaxf(M, mw[w]);
     }
+#pragma unroll
+    for (int w = 0; w < F32M_MAXW; ++w) {
+        f[w] = (w >= W || mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - M) * c);
+        L = fmaf(f[w], lw[w], L);
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    // entries in groups of 4: group gi = wave, wave + W, ... (8 groups)
     float res[32];
-    if (wave == 0) {
-        const float inv = (L > 0.f) ? 1.f / L : 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            float u = 0.f;
+    for (int gk = 0; gk < 8; ++gk) {
+        const int gi = wave + gk * W;
+        if (gi < 8) {
 #pragma unroll
-            for (int w = 0; w < F32M_MAXW; ++w)
-                if (w < W) u = fmaf(f[w], su[(w * 32 + i) * 64 + lane], u);
-            res[i] = u * inv;
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * gi + j;
+                float u = 0.f;
+#pragma unroll
+                for (int w = 0; w < F32M_MAXW; ++w) u = fmaf(f[w], su[(min(w, W - 1) * 32 + i) * 64 + lane], u);
+                res[4 * gk + j] = u * inv;
+            }
         }
     }
     __syncthreads();
-    // transpose through LDS into [row][dim] and store whole rows
+    // transpose through LDS into [row][dim] and store whole rows: entry
+    // i = 16 db + r of lane (l32, h2) is dim 32 db + 8 (r / 4) + 4 h2 + r % 4
     float* so = su;   // [32 rows][OS]
-    if (wave == 0) {
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+    for (int gk = 0; gk < 8; ++gk) {
+        const int gi = wave + gk * W;
+        if (gi < 8) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                so[l32 * OS + 32 * db + 8 * (r >> 2) + 4 * h2 + (r & 3)] = res[db * 16 + r];
-        if (lse != nullptr && h2 == 0 && myrow < N) lse[(size_t)bh * N + myrow] = (M * c + log2f(L)) * kLn2;
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * gi + j;
+                so[l32 * OS + 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h2 + (i & 3)] = res[4 * gk + j];
+            }
+        }
     }
+    if (wave == 0 && lse != nullptr && h2 == 0 && myrow < N) lse[(size_t)bh * N + myrow] = (M * c + log2f(L)) * kLn2;
     __syncthreads();
     for (int e = tid * 4; e < 32 * D; e += blockDim.x * 4) {
         const int row = e / D, col = e % D;
