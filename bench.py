@@ -198,7 +198,8 @@ def dense_kernel_name(cfg) -> str:
     if cfg.d == 64 and cfg.N <= 208 and cfg.B * cfg.Hq >= 256:
         return (f"prefill_short_kernel<{'causal' if cfg.causal else 'non-causal'}, "
                 f"{'pipelined' if cfg.N > 192 else 'staged whole'}>")
-    return f"prefill_bf16_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
+    return (f"prefill_bf16_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}, "
+            f"{32 if cfg.d == 64 else 64}-key tiles>")
 
 
 def time_dense(torch, dev, stream, cfg, steps, warmup):
