@@ -32,7 +32,9 @@
 //     exceeds it by more than 2^8 in weight does the wave rescale l and u.
 //   * Causal: tiles entirely above the diagonal are never visited, the q
 //     tiles are dispatched heaviest first, and a wave whose rows all lie
-//     before a tile skips its arithmetic for it.
+//     before a tile skips its arithmetic for it.  In the pipelined kernel
+//     the units that read one kv head stay on a subset of the XCDs
+//     (causal_unit), which halves the K/V fetched past the L2s.
 //   * Non-causal: the q tiles that read one kv head run as consecutive
 //     workgroups of one XCD, so its K/V tiles come from HBM once and from
 //     that XCD's L2 after.
@@ -549,6 +551,41 @@ prefill_short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int rb = wave + PF_WAVES; rb < n_rb; rb += PF_WAVES) row_block(std::false_type{}, rb);
 }
 
+// Causal work units (b, h, q tile), heaviest q tiles first, with the units
+// that read one kv head's K and V kept on a subset of the XCDs (workgroup w
+// runs on XCD w % 8), so that each XCD's L2 holds fewer kv heads.
+//   mode 0: unit w of the heaviest-first order (no XCD placement);
+//   mode 1 (kv heads a multiple of 8): XCD x takes kv heads x, x + 8, ...;
+//           its j-th workgroup takes the j-th of their units, heaviest first;
+//   mode 2 (8 a multiple of the kv heads): each kv head owns 8 / n_kv XCDs,
+//           which deal its units (heaviest first) round-robin; workgroups past
+//           the end of a kv head's units (grid padding) get none.
+// Returns false for a padding workgroup.
+__device__ __forceinline__ bool causal_unit(int wg, int BH, int G, int n_qtiles, int mode, int& qt, int& bh) {
+    if (mode == 0) {
+        qt = n_qtiles - 1 - wg / BH;
+        bh = wg % BH;
+        return true;
+    }
+    const int n_kv = BH / G;
+    const int x = wg & 7, j = wg >> 3;
+    if (mode == 1) {
+        const int L = (n_kv / 8) * G;     // units of one q tile index on an XCD
+        const int qi = j / L, rem = j - qi * L;
+        if (qi >= n_qtiles) return false;
+        qt = n_qtiles - 1 - qi;
+        bh = (x + 8 * (rem / G)) * G + rem % G;
+        return true;
+    }
+    const int S = 8 / n_kv;
+    const int r = x / S;
+    const int u = j * S + (x - r * S);
+    if (u >= G * n_qtiles) return false;
+    qt = n_qtiles - 1 - u / G;
+    bh = r * G + u % G;
+    return true;
+}
+
 // Software-pipelined variant: inside each wave, the vector work of key
 // tile j runs between the matrix instructions of its neighbours, because a
 // wave's own independent VALU instructions issue while its MFMAs execute
@@ -568,7 +605,7 @@ __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu
 prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                   float* __restrict__ lse, int Hq, int Hkv, int N, int BH, int n_qtiles,
-                  float c, int negate) {
+                  float c, int negate, int xcd_map) {
     constexpr int CPR = D / 8;
     constexpr int TILE = PF_BN * D;
     constexpr int LINST = PF_BN * CPR / PF_THREADS;
@@ -584,10 +621,8 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const int lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, l32 = lane & 31;
 
-    // Work unit: (b, h, q tile); heaviest q tiles first when causal.
-    const int wg = blockIdx.x;
-    const int qt = CAUSAL ? (n_qtiles - 1 - wg / BH) : (wg / BH);
-    const int bh = wg % BH;
+    int qt, bh;
+    if (!causal_unit((int)blockIdx.x, BH, Hq / Hkv, n_qtiles, xcd_map, qt, bh)) return;
     const int b = bh / Hq, h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
     const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -769,10 +804,28 @@ hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         // can compare the two
         const char* plain = getenv("ATTN_PREFILL_PLAIN");
         if (a.c > 0.f && !bn_forced && !(plain != nullptr && plain[0] == '1')) {
-            hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), grid, block, 0, stream,
+            // XCD placement of the units by kv head (causal_unit); the grid of
+            // mode 2 is padded to 8 equal XCD shares.  ATTN_PREFILL_XCD=0
+            // (test hook) places them in plain heaviest-first order.
+            const int G = a.Hq / a.Hkv, n_kv = BH / G;
+            const char* xe = getenv("ATTN_PREFILL_XCD");
+            int mode = 0;
+            long long ngrid = (long long)BH * n_qt;
+            if (!(xe != nullptr && xe[0] == '0')) {
+                if (n_kv % 8 == 0) {
+                    mode = 1;
+                } else if (8 % n_kv == 0) {
+                    const long long S = 8 / n_kv, per = ((long long)G * n_qt + S - 1) / S;
+                    if (8 * per < (1LL << 31)) {
+                        mode = 2;
+                        ngrid = 8 * per;
+                    }
+                }
+            }
+            hipLaunchKernelGGL((prefill_sp_kernel<D, CAUSAL>), dim3((unsigned)ngrid), block, 0, stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                               a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate);
+                               a.Hq, a.Hkv, a.N, BH, n_qt, a.c, a.negate, mode);
             return hipGetLastError();
         }
     }

@@ -288,6 +288,31 @@ def test_pipelined_matches_plain(monkeypatch, B, Hq, Hkv, N):
     assert max_abs(f64(o1), ro) <= O_TOL[torch.bfloat16]
 
 
+# (B, Hq, Hkv, N) by placement: kv heads a multiple of 8 (each XCD its own kv
+# heads), 8 a multiple of the kv heads (each kv head on 8 / n_kv XCDs; with
+# and without padding workgroups), and neither (plain heaviest-first order).
+XCD_CASES = [(8, 2, 1, 300), (1, 16, 16, 200), (2, 8, 8, 129), (1, 12, 2, 1000), (1, 6, 1, 300),
+             (1, 12, 4, 333), (1, 6, 3, 200), (3, 2, 1, 400)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", XCD_CASES)
+def test_causal_xcd_placement(monkeypatch, B, Hq, Hkv, N):
+    """The causal d = 128 units are placed on the XCDs by kv head; every
+    (head, q tile) must still be computed exactly once, against its own kv
+    head: the result must equal, bit for bit, the launch in plain
+    heaviest-first order (ATTN_PREFILL_XCD=0), and match the oracle."""
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=128, dtype="bf16", seed=300 + N + Hq)
+    scale = 1.0 / math.sqrt(128)
+    o1, l1 = run_fwd(q, k, v, scale, True)
+    monkeypatch.setenv("ATTN_PREFILL_XCD", "0")
+    o2, l2 = run_fwd(q, k, v, scale, True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), scale, True)
+    assert max_abs(f64(o1), ro) <= O_TOL[torch.bfloat16]
+    assert max_abs(l1.double().numpy(), rl) <= LSE_TOL
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 12, 2, 1000), (2, 4, 4, 333), (1, 2, 1, 31), (8, 2, 1, 300)])
