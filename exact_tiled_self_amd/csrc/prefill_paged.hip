@@ -18,13 +18,17 @@
 // 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in
 // LDS, K and V loaded straight into LDS, MFMA 32x32x16 bf16
 // on S^T = K Q^T and O^T += V^T P^T, lazy rescale of the running maximum.
-// The work units are (query tile, sequence, query head), heads fastest.
-// Sequence lengths vary widely, so the (query tile, sequence) pairs run
-// longest first: every workgroup ranks the pairs by the number of keys their
-// last row sees, read from the device-resident lengths (up to 512 pairs;
-// beyond that, later query tiles first).  The block -> unit map sends the
-// heads that share a kv head to one XCD, side by side, so they share its
-// tiles in that XCD's L2.
+// The work is cut into items: a run of up to cq consecutive query tiles of
+// one sequence (a chunk) for one kv head, i.e. cq x G workgroups, one per
+// (query tile, query head) of the chunk.  All workgroups of an item run on
+// one XCD, side by side, so they read the chunk's keys and values from that
+// XCD's L2 instead of each fetching them from HBM.  Sequence lengths vary
+// widely, so the chunks run longest first: every workgroup ranks them by the
+// keys their query tiles see, read from the device-resident lengths (up to
+// 512 chunks; beyond that, later chunks first), and the ranked items are
+// dealt to the 8 XCDs in a serpentine order, so each XCD gets a like share.
+// The launch picks cq so that every XCD still gets at least 8 items and one
+// item fits on an XCD at once.
 //
 // Device-resident values are checked before they form an address: a
 // sequence with malformed row offsets (or more than max_new rows) is left
@@ -32,15 +36,20 @@
 // gets NaN rows; a row that attends to a block with an out-of-range table
 // entry gets NaN.
 
+#include <algorithm>
+#include <cstdlib>
+
 #include "internal.h"
 #include "prefill_tile.h"
 
 namespace attn {
 namespace {
 
-// Up to this many (q tile, sequence) pairs, every workgroup ranks them by
-// cost to run the longest first (P^2 / 256 comparisons per thread).
+// Up to this many chunks, every workgroup ranks them by cost to run the
+// longest first (P^2 / 256 comparisons per thread).
 constexpr int kRankPairs = 512;
+// An item (cq x G workgroups) fits on one XCD: 32 CUs x 2 workgroups.
+constexpr int kItemUnits = 64;
 constexpr uint32_t kNaNBf16x2 = 0x7FC07FC0u;   // two quiet bf16 NaNs
 constexpr uint32_t kNaN32 = 0x7FC00000u;       // quiet fp32 NaN
 
@@ -50,15 +59,15 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
                      const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ starts,
                      uint16_t* __restrict__ o, float* __restrict__ lse, int S, int T, int max_new,
-                     int Hq, int Hkv, int max_blocks, int num_blocks, int n_qtiles, float c,
-                     int negate) {
+                     int Hq, int Hkv, int max_blocks, int num_blocks, int n_qtiles, int cq,
+                     float c, int negate) {
     using L = PfLayout<D>;
     constexpr int BS = kDecodeBlock;
     static_assert(PF_BN == PF_WAVES * BS, "one cache block per wave per key tile");
     __shared__ __attribute__((aligned(16))) uint16_t smem0[L::BUF];
     __shared__ __attribute__((aligned(16))) uint16_t smem1[L::BUF];
     __shared__ int bad_s[PF_WAVES];
-    __shared__ int rank_cost[kRankPairs];
+    __shared__ long long rank_cost[kRankPairs];
     __shared__ int rank_pick;
 
     const int tid = threadIdx.x;
@@ -66,47 +75,57 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
 
-    // Work unit: (q tile, sequence, head), latest q tiles first, heads
-    // fastest.  Workgroup b runs on XCD b % 8; the j-th workgroup of XCD x
-    // takes unit (j / G) * 8G + x * G + j % G, so the G heads that share a kv
-    // head (one aligned run of G units) run on one XCD and share its L2.
+    // Workgroup b runs on XCD b % 8.  The k-th item of XCD x is item slot
+    // 8k + x (k even) or 8k + 7 - x (k odd); slot = rank * Hkv + kv head, rank
+    // in the longest-first order of the chunks.  Within an item, later query
+    // tiles first, the G query heads of the kv head side by side.
     const int G = Hq / Hkv;
+    const int U = cq * G;                                     // workgroups per item
+    const int n_ch = (n_qtiles + cq - 1) / cq;                // chunks per sequence
+    const int P = n_ch * S;                                   // chunks
     const int xcd = blockIdx.x & (kXcds - 1), jx = blockIdx.x / kXcds;
-    const int wg = (jx / G) * (kXcds * G) + xcd * G + jx % G;
-    const int SH = S * Hq;
-    if (wg >= n_qtiles * SH) return;
-    const int h = wg % Hq, g = h / G;
-    int qt, s;
-    const int P = n_qtiles * S;                               // (q tile, sequence) pairs
+    const int k = jx / U, e = jx - k * U;
+    const int slot = k * kXcds + ((k & 1) ? kXcds - 1 - xcd : xcd);
+    if (slot >= P * Hkv) return;
+    const int rank = slot / Hkv, g = slot - rank * Hkv;
+    const int h = g * G + e % G;
+    int ch, s;
     if (P <= kRankPairs) {
-        // Longest first: the pair of rank wg / Hq in decreasing order of the
-        // keys its last row sees (ties by pair index), from the lengths.
+        // Longest first: the chunk of rank `rank` in decreasing order of the
+        // keys its query tiles see (ties by chunk index), from the lengths.
         for (int i = tid; i < P; i += PF_THREADS) {
-            const int qi = i / S, si = i - qi * S;
-            const int ai = starts[si], bi = starts[si + 1], ci = ctx_lens[si];
+            const int ci_ = i / S, si = i - ci_ * S;
+            const int ai = starts[si], bi = starts[si + 1], li = ctx_lens[si];
             const int ni = bi - ai;
-            const bool runs = !(ai < 0 || bi > T || ni < 0 || ni > max_new) && qi * PF_BM < ni;
-            const bool sane = ci >= ni && ci <= max_blocks * kDecodeBlock;
-            rank_cost[i] = !runs ? -1 : (sane ? ci - ni + min(qi * PF_BM + PF_BM, ni) : 0);
+            const bool runs = !(ai < 0 || bi > T || ni < 0 || ni > max_new) && ci_ * cq * PF_BM < ni;
+            const bool sane = li >= ni && li <= max_blocks * kDecodeBlock;
+            long long cost = -1;
+            if (runs) {
+                cost = 0;
+                const int t_end = min(ci_ * cq + cq, (ni + PF_BM - 1) / PF_BM);
+                if (sane)
+                    for (int t = ci_ * cq; t < t_end; ++t) cost += li - ni + min(t * PF_BM + PF_BM, ni);
+            }
+            rank_cost[i] = cost;
         }
         __syncthreads();
-        const int want = wg / Hq;
         for (int i = tid; i < P; i += PF_THREADS) {
-            const int ci = rank_cost[i];
+            const long long ci = rank_cost[i];
             int r = 0;
             for (int j = 0; j < P; ++j) {
-                const int cj = rank_cost[j];
+                const long long cj = rank_cost[j];
                 r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
             }
-            if (r == want) rank_pick = i;
+            if (r == rank) rank_pick = i;
         }
         __syncthreads();
-        qt = rank_pick / S;
-        s = rank_pick - qt * S;
+        ch = rank_pick / S;
+        s = rank_pick - ch * S;
     } else {
-        qt = n_qtiles - 1 - wg / SH;                          // later q tiles first
-        s = (wg - (wg / SH) * SH) / Hq;
+        ch = n_ch - 1 - rank / S;                             // later chunks first
+        s = rank - (rank / S) * S;
     }
+    const int qt = ch * cq + cq - 1 - e / G;                  // later q tiles first
 
     const int a = starts[s], b = starts[s + 1], ctx = ctx_lens[s];
     const int n = b - a;
@@ -255,14 +274,30 @@ prefill_paged_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 template <int D>
 hipError_t launch_paged_prefill_t(const PagedPrefillArgs& a, hipStream_t stream) {
     const int n_qt = (a.max_new + PF_BM - 1) / PF_BM;
-    const long long units = (long long)n_qt * a.S * a.Hq;
-    const long long per_round = (long long)kXcds * (a.Hq / a.Hkv);      // whole runs on every XCD
-    const dim3 grid((unsigned)((units + per_round - 1) / per_round * per_round)), block(PF_THREADS);
+    const int G = a.Hq / a.Hkv;
+    // Query tiles per item: as many as fit on one XCD (kItemUnits
+    // workgroups), while the items still number at least 8 per XCD.
+    // ATTN_PAGED_CQ=<n> (test hook) forces another cut, which must give the
+    // same result bit for bit.
+    int cq = std::max(1, std::min(n_qt, kItemUnits / G));
+    while (cq > 1 && (long long)a.S * ((n_qt + cq - 1) / cq) * a.Hkv < 8LL * kXcds) --cq;
+    if (const char* env = getenv("ATTN_PAGED_CQ")) {
+        const int f = atoi(env);
+        if (f >= 1 && f <= std::max(n_qt, 1)) cq = f;
+    }
+    auto grid_of = [&](int q) {
+        const long long slots = (long long)((n_qt + q - 1) / q) * a.S * a.Hkv;
+        return (slots + kXcds - 1) / kXcds * kXcds * q * G;
+    };
+    // (one tile per item always fits: the entry point bounds n_qt * S * Hq)
+    if (grid_of(cq) >= (1LL << 31)) cq = 1;
+    const long long ngrid = grid_of(cq);
+    const dim3 grid((unsigned)ngrid), block(PF_THREADS);
     hipLaunchKernelGGL((prefill_paged_kernel<D>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, a.starts,
                        static_cast<uint16_t*>(a.o), a.lse, a.S, a.T, a.max_new, a.Hq, a.Hkv,
-                       a.max_blocks, a.num_blocks, n_qt, a.c, a.negate);
+                       a.max_blocks, a.num_blocks, n_qt, cq, a.c, a.negate);
     return hipGetLastError();
 }
 

@@ -300,3 +300,37 @@ def test_deterministic():
     o1, l1 = gpu_prefill(p, 0.0884)
     o2, l2 = gpu_prefill(p, 0.0884)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def _lens(seed, S, new_hi, extra_hi):
+    rng = np.random.default_rng(seed)
+    new = rng.integers(1, new_hi + 1, S)
+    return [int(n + e) for n, e in zip(new, rng.integers(0, extra_hi + 1, S))], [int(n) for n in new]
+
+
+# (d, Hq, Hkv, S, most new rows, most earlier context): the automatic cut puts
+# 3 query tiles in an item for the first three, 2 for the fourth; the last
+# has more than 512 chunks (no cost ranking: later chunks first).
+CUT_CASES = [(128, 8, 8, 10, 300, 400), (128, 12, 2, 40, 300, 300), (64, 16, 1, 70, 300, 200),
+             (128, 12, 2, 33, 256, 500), (64, 12, 2, 520, 2, 40)]
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,S,new_hi,extra_hi", CUT_CASES)
+def test_item_cuts(monkeypatch, d, Hq, Hkv, S, new_hi, extra_hi):
+    """The work is cut into items of up to cq query tiles of one sequence and
+    kv head, each item on one XCD: every cut (ATTN_PAGED_CQ) gives the same
+    bits, and the automatic one matches the oracle."""
+    ctx, new = _lens(S * Hq + d, S, new_hi, extra_hi)
+    p = chunked_inputs(cfg(Hq, Hkv, d), S=S, ctx_lens=ctx, new_lens=new, poison=True,
+                       max_blocks=(max(ctx) + 15) // 16 + 1, seed=S + d)
+    sc = 1.0 / math.sqrt(d)
+    o, lse = gpu_prefill(p, sc)
+    n_qt = (p["max_new"] + 127) // 128
+    for cq in sorted({1, 2, n_qt} & set(range(1, n_qt + 1))):
+        monkeypatch.setenv("ATTN_PAGED_CQ", str(cq))
+        o2, l2 = gpu_prefill(p, sc)
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), f"o differs at cq={cq}"
+        assert torch.equal(lse.view(torch.int32), l2.view(torch.int32)), f"lse differs at cq={cq}"
+    monkeypatch.delenv("ATTN_PAGED_CQ")
+    ro, rl = oracle_prefill(p, sc)
+    assert_close(o, lse, ro, rl, name=f"cuts d{d} {Hq}/{Hkv} S={S}")
