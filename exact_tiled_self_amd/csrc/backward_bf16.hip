@@ -22,7 +22,8 @@
 //     key, its K (and V) rows stay in registers.  The dV pass computes
 //     S = Q K^T, P and dV^T += dO^T P; the dK pass S, dP = dO V^T,
 //     dS = P (dP - D) and dK^T += Q^T dS.  Q, dO, lse and D go straight to
-//     LDS in a ring of three chunks; dO^T and Q^T come from transpose loads.
+//     LDS in a ring of three chunks, last chunk first; dO^T and Q^T come
+//     from transpose loads.
 //   * bwd_reduce: with grouped K/V heads the two passes write one fp32
 //     dk, dv per query head into the workspace and this kernel sums each
 //     group in head order into the bf16 outputs.
@@ -391,20 +392,25 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
     const int nq = n_c - c_first;                    // >= 1 (key0 < N)
-    issue_loads(c_first, ring0);
-    if (nq > 1) issue_loads(c_first + 1, ring1);
+    // Chunks are taken from the last one back to c_first: the workgroups of
+    // a head's key tiles then read the same q and dout rows at about the same
+    // time (the later key tiles simply stop sooner), so those rows come from
+    // the L2 for all but the first of them.
+    issue_loads(n_c - 1, ring0);
+    if (nq > 1) issue_loads(n_c - 2, ring1);
 
-    // chunk t of the ring: wait for its loads (those of chunk t+1 may stay in
-    // flight), barrier, start chunk t+2 into the buffer chunk t-1 used, compute
+    // step t of the ring (chunk n_c-1-t): wait for its loads (those of the
+    // next step may stay in flight), barrier, start step t+2's chunk into the
+    // buffer step t-1 used, compute
     auto step = [&](int t, const uint16_t* base, uint16_t* nxt2) {
-        const int cj = c_first + t;
+        const int cj = n_c - 1 - t;
         if (t + 1 < nq) wait_vmcnt<OPS>(); else wait_vmcnt<0>();
         // a plain barrier (no fence, which would drain every load in flight);
         // the memory clobber keeps the compiler from moving LDS accesses
         // across it, and every LDS read of the previous chunk has been
         // consumed by its MFMAs before a wave gets here
         asm volatile("s_barrier" ::: "memory");
-        if (t + 2 < nq) issue_loads(cj + 2, nxt2);
+        if (t + 2 < nq) issue_loads(cj - 2, nxt2);
         const int qc = cj * BW_T;
         // skip a chunk whose queries all precede this wave's keys
         if (wave_active && (!CAUSAL || qc + BW_T - 1 >= wkey0)) {
