@@ -8,7 +8,10 @@
 // section "No basta con promediar los resultados de los bloques"): scores of
 // the tile, new running maximum, rescale of l and u by e^(m - m') when it
 // rises, P = e^(s - m), l += rowsum P, u += P V.  Scores are in base 2 with
-// c = |scale| * log2(e).
+// c = |scale| * log2(e).  The maximum moves lazily (only by more than 2^8 in
+// weight), and the tile's weights, taken against the running maximum first,
+// show through their row sums whether it could move at all: only then is the
+// tile's maximum formed.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 on the TRANSPOSED products: S^T = K Q^T puts
 // one query row per lane (lane % 32) with 16 of its keys per 32-key block,
@@ -78,6 +81,10 @@ __device__ __forceinline__ int pf_vtr_offset(int lane, int db) {
 // reference (weights up to 256 are exact in fp32 and bf16 range) and the
 // numerator needs no rescale.  u / l is unchanged by the choice of reference.
 constexpr float kLazyLog2 = 8.0f;
+// The quick form of that test (one lane's part of a row sum of weights at
+// most 2^7): it implies the full test's answer with a margin of one in the
+// exponent, far above the rounding of either side.
+constexpr float kLazyCheck = 128.0f;
 
 // Advance one wave's rows over the tile of keys k0 .. k0 + BN - 1 staged at
 // Ks (K) and Vs (V, row-major).  BN (keys per tile) is 64, or 32 for a
@@ -133,83 +140,104 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
         }
     };
 
-    // S^T = K Q^T for the 64 keys of this tile (two 32-key blocks).
+    // S^T = K Q^T for the keys of this tile (32-key blocks).
     f32x16 sacc[BN / 32];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KPF; ++ks) kread(ks);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (ks + KPF < KS) kread(ks + KPF);
-        __builtin_amdgcn_sched_barrier(0);
+    auto scores = [&]() {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KPF; ++ks) kread(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + KPF < KS) kread(ks + KPF);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Lane key of accumulator entry r in block kb: k0 + 32kb + 8(r/4) + 4hi + r%4.
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool ok = key < kend && (!CAUSAL || key <= mypos);
+                    sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+                }
+        }
+    };
+    // P = 2^(c s - mc) in place, and this lane's part of the row sum.
+    auto weights = [&](float mc) {
+        float lsum = 0.f;
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float sv = sacc[kb][r];
+                    const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+                    sacc[kb][r] = p;
+                    lsum += p;
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
+                    sacc[kb][r] = p;
+                    lsum += p;
+                }
+        }
+        return lsum;
+    };
+    scores();
 
     // The first V^T operands are read now; the softmax below hides them.
     bf16x8 va[2][D / 32];
     vread(0, va[0]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // Lane key of accumulator entry r in block kb: k0 + 32kb + 8(r/4) + 4hi + r%4.
-    float mx = kNegInf;
-    if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const bool ok = key < kend && (!CAUSAL || key <= mypos);
-                sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
-                mx = fmaxf(mx, sacc[kb][r]);
-            }
-    } else {
+    // Once every row has a running maximum, the weights are taken against it
+    // directly.  A lane's part of a row sum bounds each of its weights, so
+    // when no part exceeds 2^kLazyCheckLog2 no score rose above the running
+    // maximum by 2^kLazyCheckLog2 in weight, fewer than the 2^kLazyLog2 that
+    // would move it: the tile keeps the maximum, exactly as the full test
+    // below decides.  Otherwise (rare after the first tile: a part that
+    // large) the scores are computed again and take the full test.
+    bool full = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0;
+    float lsum = 0.f;
+    if (!full) {
+        lsum = weights(m_run * c);
+        full = __builtin_amdgcn_ballot_w64(!(lsum <= kLazyCheck)) != 0;
+        if (full) scores();
+    }
+    if (full) {
+        float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    }
-    mx = max_halves(mx);
+        mx = max_halves(mx);
 
-    // Lazy rescale: a wave-uniform branch taken only when some row's
-    // maximum grew by more than 2^kLazyLog2 (always on the first tile).
-    const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
-        l_run *= alpha;
+        // Lazy rescale: a wave-uniform branch taken only when some row's
+        // maximum grew by more than 2^kLazyLog2 (always on the first tile).
+        const bool grow = (m_run == kNegInf) ? (mx != kNegInf) : ((mx - m_run) * c > kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-    }
-    const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-    float lsum = 0.f;
-    if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float sv = sacc[kb][r];
-                const float p = (sv == kNegInf) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
-                sacc[kb][r] = p;
-                lsum += p;
-            }
-    } else {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
-                sacc[kb][r] = p;
-                lsum += p;
-            }
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        lsum = weights((m_run == kNegInf) ? 0.f : m_run * c);
     }
     l_run += lsum;
     __builtin_amdgcn_sched_barrier(0);
