@@ -334,3 +334,27 @@ def test_item_cuts(monkeypatch, d, Hq, Hkv, S, new_hi, extra_hi):
     monkeypatch.delenv("ATTN_PAGED_CQ")
     ro, rl = oracle_prefill(p, sc)
     assert_close(o, lse, ro, rl, name=f"cuts d{d} {Hq}/{Hkv} S={S}")
+
+
+@pytest.mark.parametrize("step", [4.5, 7.0, -3.0])
+def test_rescale_quick_test_fallback(step):
+    """Scores that climb (or fall) from one 32-position block of the context
+    to the next and are equal inside a block: the tile step's quick row-sum
+    test fails on every tile (or never after the first), so the exact-maximum
+    path runs after it; every row against the oracle."""
+    ctx = [300, 130, 64, 200]
+    new = [300, 40, 64, 1]
+    p = chunked_inputs(cfg(), S=len(ctx), ctx_lens=ctx, new_lens=new, poison=True, max_blocks=20,
+                       seed=int(10 * abs(step)) + (7 if step < 0 else 5))
+    p["q_new"].zero_()
+    p["q_new"][..., 0] = 1.0
+    kc = p["k_cache"]
+    table = p["block_table"].numpy()
+    for s, n in enumerate(ctx):
+        for t in range(n):
+            blk, slot = int(table[s, t // 16]), t % 16
+            kc[blk, :, slot, :] = 0.0
+            kc[blk, :, slot, 0] = step * (t // 32)
+    o, lse = gpu_prefill(p, 1.0)
+    ro, rl = oracle_prefill(p, 1.0)
+    assert_close(o, lse, ro, rl, name=f"staircase step {step}")

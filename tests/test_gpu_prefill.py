@@ -443,3 +443,36 @@ def test_long_prefill_allocates_nothing():
     assert torch.cuda.max_memory_allocated() == peak0
     assert abs(torch.cuda.mem_get_info()[0] - free0) < (64 << 20)
     assert torch.isfinite(o[0, :, -1].float()).all()
+
+
+def staircase_inputs(N, d, step, seed):
+    """One head whose scores climb by `step` (natural-log units at scale 1)
+    from one 32-key block to the next and are equal inside a block, so that
+    every lane's part of a row sum of weights exceeds 2^7 while the running
+    maximum rises by less or more than 2^8 in weight from tile to tile."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.zeros(1, 1, N, d)
+    k = torch.zeros(1, 1, N, d)
+    q[..., 0] = 1.0
+    k[0, 0, :, 0] = step * (torch.arange(N) // 32).float()
+    v = torch.randn(1, 1, N, d, generator=g)
+    return tuple(t.to(torch.bfloat16) for t in (q, k, v))
+
+
+@pytest.mark.parametrize("d,bn", [(64, "32"), (64, "64"), (128, "32"), (128, "64")])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("step", [4.5, 7.0, -3.0])
+def test_rescale_quick_test_fallback(monkeypatch, d, bn, causal, step):
+    """The tile step first takes a tile's weights against the running maximum
+    and forms the tile maximum only when a row-sum part exceeds 2^7; these
+    inputs make that happen on every tile (steps of 4.5 and 7 in natural
+    units: growths of 6.5 and 10 in base 2, below and above the lazy
+    threshold of 8), or never after the first (falling scores), on both tile
+    sizes of the plain kernel; every element against the oracle."""
+    monkeypatch.setenv("ATTN_PREFILL_BN", bn)
+    q, k, v = staircase_inputs(300, d, step, seed=int(10 * step) + d)
+    o, lse = run_fwd(q, k, v, 1.0, causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), 1.0, causal)
+    assert max_abs(f64(o), ro) <= O_TOL[torch.bfloat16]
+    assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
