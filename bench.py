@@ -191,7 +191,7 @@ def plain_copy(torch, dev, mib):
 def dense_kernel_name(cfg) -> str:
     if cfg.dtype == "f32":
         if cfg.d == 64:
-            return f"prefill_f32_mfma_kernel<{'causal' if cfg.causal else 'non-causal'}>"
+            return f"prefill_f32_mfma16_kernel<{'causal' if cfg.causal else 'non-causal'}>"
         return f"prefill_f32_kernel<{cfg.d}, {'causal' if cfg.causal else 'non-causal'}>"
     if cfg.d == 128 and cfg.causal:
         return f"prefill_sp_kernel<{cfg.d}, causal>"

@@ -13,6 +13,8 @@
 // stays within a few fp32 ulps of the exact one.
 
 #include "common.h"
+#include <stdlib.h>
+
 #include "internal.h"
 
 namespace attn {
@@ -377,6 +379,182 @@ prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k
     }
 }
 
+// The same on 16-row query blocks (v_mfma_f32_16x16x4f32: twice the
+// workgroups, each wave's products half as long).  A workgroup owns one
+// 16-row block of one head; its W waves take the head's 32-key blocks in turn
+// and the partial states are merged through LDS as above.  Per 32-key block,
+// two 16-key halves h:
+//   * S^T = K Q^T: at step s lane l gives K[key 16h + l % 16][dim 16 (l / 16)
+//     + s] and Q[row l % 16][the same dim] (each lane group walks its own 16
+//     dims); lane l gets back the scores of row l % 16 with keys
+//     16h + 4 (l / 16) + r, r = 0..3.
+//   * O^T += V^T P^T, one product per (h, r) and 16-dim block db: step (h, r)
+//     pairs key 16h + 4 (l / 16) + r with lane group l / 16, which is the
+//     lane's own score entry, so P^T is the lane's weights in order and V^T is
+//     V[that key][dim 16 db + l % 16]; lane l gets back dims
+//     16 db + 4 (l / 16) + r' of row l % 16.
+template <bool CAUSAL>
+__global__ void __launch_bounds__(64 * F32M_MAXW)
+prefill_f32_mfma16_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+                          float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, int BH,
+                          int n_qb, float c, int negate) {
+    constexpr int D = 64;
+    // partial states: u[w][entry][lane] (lane fastest: no bank conflicts),
+    // then m and l per (w, row)
+    __shared__ __attribute__((aligned(16))) float su[F32M_MAXW * 16 * 64];
+    __shared__ float sm[F32M_MAXW * 16], sl[F32M_MAXW * 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int W = blockDim.x >> 6;
+    const int grp = lane >> 4, l16 = lane & 15;
+    const int wg = blockIdx.x;
+    const int qb = CAUSAL ? (n_qb - 1 - wg / BH) : (wg / BH);
+    const int bh = wg % BH;
+    const int b = bh / Hq, h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    const uint32_t head_bytes = (uint32_t)N * D * 4;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (size_t)bh * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((size_t)b * Hkv + g) * N * D, head_bytes);
+    const int q0 = qb * 16;
+    const int myrow = q0 + l16;
+    const int n_kb = CAUSAL ? min((q0 + 15) / 32 + 1, (N + 31) / 32) : (N + 31) / 32;
+
+    // q: row l16, dims 16 grp .. 16 grp + 15 (zero past N)
+    float qv[16];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+        const f32x4 x = __builtin_bit_cast(f32x4, buf_ld16(qrs, (uint32_t)(myrow * D + 16 * grp + i) * 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[i + j] = x[j];
+    }
+
+    f32x4 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+
+    for (int kb = wave; kb < n_kb; kb += W) {
+        const int k0 = kb * 32;
+        // K rows k0 + 16 hh + l16, dims 16 grp ..; V of the pairing, dims 16 db + l16
+        float kv[2][16], vv[2][4][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const f32x4 x = __builtin_bit_cast(
+                    f32x4, buf_ld16(krs, (uint32_t)((k0 + 16 * hh + l16) * D + 16 * grp + i) * 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kv[hh][i + j] = x[j];
+            }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const int key = k0 + 16 * hh + 4 * grp + r;
+                    vv[hh][r][db] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                  vrs, (uint32_t)(key * D + 16 * db + l16) * 4, 0, 0));
+                }
+        // every load of the block is issued before the first product uses one
+        __builtin_amdgcn_sched_barrier(0);
+
+        // the two halves are independent accumulator chains
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int st = 0; st < 16; ++st)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[hh][st], qv[st], sacc[hh], 0, 0, 0);
+        if (negate) {
+            sacc[0] = -sacc[0];   // (-q).k, exactly
+            sacc[1] = -sacc[1];
+        }
+
+        // mask, row maximum (the row's 32 keys: 8 in each of lanes l16 + 16 grp)
+        float mx = kNegInf;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + 16 * hh + 4 * grp + r;
+                const bool ok = key < N && (!CAUSAL || key <= myrow);
+                sacc[hh][r] = ok ? sacc[hh][r] : kNegInf;
+                mx = fmaxf(mx, sacc[hh][r]);
+            }
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_use) * c);
+        float lsum = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = (sacc[hh][r] == kNegInf) ? 0.f : fast_exp2((sacc[hh][r] - m_use) * c);
+                sacc[hh][r] = p;
+                lsum += p;
+            }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[hh][r][db], sacc[hh][r], oacc[db], 0, 0, 0);
+        m_run = m_new;
+    }
+    // the row's sum over its four lane groups
+    l_run += xor_shfl(l_run, 16);
+    l_run += xor_shfl(l_run, 32);
+
+    // merge the W partial states of each row through LDS
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) su[(wave * 16 + db * 4 + r) * 64 + lane] = oacc[db][r];
+    if (grp == 0) {
+        sm[wave * 16 + l16] = m_run;
+        sl[wave * 16 + l16] = l_run;
+    }
+    __syncthreads();
+    // Every wave forms the weights e^(m_w - M) of its lanes' rows; wave db
+    // (< 4) merges the four entries of dims block db and stores them as one
+    // 16-byte run per lane.  (Branch-free: state w >= W reads state W - 1 with
+    // weight 0.)
+    float M = kNegInf, L = 0.f;
+    float f[F32M_MAXW], mw[F32M_MAXW], lw[F32M_MAXW];
+#pragma unroll
+    for (int w = 0; w < F32M_MAXW; ++w) {
+        const int wc = min(w, W - 1);
+        mw[w] = sm[wc * 16 + l16];
+        lw[w] = sl[wc * 16 + l16];
+        M = fmaxf(M, mw[w]);
+    }
+#pragma unroll
+    for (int w = 0; w < F32M_MAXW; ++w) {
+        f[w] = (w >= W || mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - M) * c);
+        L = fmaf(f[w], lw[w], L);
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    for (int db = wave; db < 4; db += W) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int w = 0; w < F32M_MAXW; ++w) u[r] = fmaf(f[w], su[(min(w, W - 1) * 16 + db * 4 + r) * 64 + lane], u[r]);
+        if (myrow < N)
+            *reinterpret_cast<f32x4*>(o + ((size_t)bh * N + myrow) * D + 16 * db + 4 * grp) = u * inv;
+    }
+    if (wave == 0 && lse != nullptr && grp == 0 && myrow < N) lse[(size_t)bh * N + myrow] = (M * c + log2f(L)) * kLn2;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.Hq;
@@ -393,11 +571,29 @@ hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 128) return a.causal ? launch_f32_t<128, true>(a, stream) : launch_f32_t<128, false>(a, stream);
-    // d = 64: the matrix-core kernel, one 32-row block per workgroup and at
-    // most 8 waves over the key blocks
+    // d = 64: the matrix-core kernel, one 16-row block per workgroup and at
+    // most 8 waves over the 32-key blocks (ATTN_F32_ROWS=32, a test hook: the
+    // 32-row kernel, another partition of the rows and keys)
     const int BH = a.B * a.Hq;
-    const int n_qb = (a.N + 31) / 32;
-    const int W = min(F32M_MAXW, n_qb);
+    const int n_kb = (a.N + 31) / 32;
+    const int W = min(F32M_MAXW, n_kb);
+    const char* rows_env = getenv("ATTN_F32_ROWS");
+    if (!(rows_env != nullptr && rows_env[0] == '3' && rows_env[1] == '2')) {
+        const int n_qb16 = (a.N + 15) / 16;
+        const dim3 grid16((unsigned)(BH * n_qb16)), block16((unsigned)(64 * W));
+        if (a.causal)
+            hipLaunchKernelGGL((prefill_f32_mfma16_kernel<true>), grid16, block16, 0, stream,
+                               static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                               static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Hq, a.Hkv, a.N,
+                               BH, n_qb16, a.c, a.negate);
+        else
+            hipLaunchKernelGGL((prefill_f32_mfma16_kernel<false>), grid16, block16, 0, stream,
+                               static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                               static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Hq, a.Hkv, a.N,
+                               BH, n_qb16, a.c, a.negate);
+        return hipGetLastError();
+    }
+    const int n_qb = n_kb;
     const dim3 grid((unsigned)(BH * n_qb)), block((unsigned)(64 * W));
     if (a.causal)
         hipLaunchKernelGGL((prefill_f32_mfma_kernel<true>), grid, block, 0, stream, static_cast<const float*>(a.q),

@@ -339,6 +339,26 @@ def test_second_tile_config(monkeypatch, d, causal, B, Hq, Hkv, N):
     assert max_abs(l1.double().numpy(), l2.double().numpy()) <= LSE_TOL
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 12, 12, 196), (2, 4, 2, 333), (1, 2, 1, 17), (3, 2, 2, 100)])
+def test_fp32_row_partitions(monkeypatch, causal, B, Hq, Hkv, N):
+    """The fp32 d = 64 path on 16-row query blocks (default) and on 32-row
+    blocks (ATTN_F32_ROWS=32): another partition of the rows and of the
+    merged key blocks; both against the oracle at the fp32 bound, each
+    deterministic."""
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=64, dtype="f32", seed=700 + N)
+    scale = 0.125
+    o1, l1 = run_fwd(q, k, v, scale, causal)
+    o1b, l1b = run_fwd(q, k, v, scale, causal)
+    monkeypatch.setenv("ATTN_F32_ROWS", "32")
+    o2, l2 = run_fwd(q, k, v, scale, causal)
+    assert torch.equal(o1, o1b) and torch.equal(l1, l1b)
+    ro, rl = OA.attention(f64(q), f64(k), f64(v), scale, causal)
+    for o, lse in ((o1, l1), (o2, l2)):
+        assert max_abs(f64(o), ro) <= O_TOL[torch.float32]
+        assert max_abs(lse.double().numpy(), rl) <= LSE_TOL
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,Hq,Hkv,N", [(8, 2, 1, 300), (4, 6, 2, 129), (2, 8, 8, 64), (1, 16, 8, 200)])
 def test_xcd_runs_cover_every_tile(d, B, Hq, Hkv, N):
