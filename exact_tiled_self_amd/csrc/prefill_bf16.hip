@@ -590,16 +590,20 @@ __device__ __forceinline__ bool causal_unit(int wg, int BH, int G, int n_qtiles,
 // tile j runs between the matrix instructions of its neighbours, because a
 // wave's own independent VALU instructions issue while its MFMAs execute
 // (the matrix core and the vector unit then work at once), which two
-// separate waves on a SIMD do not achieve.  Per tile j, after the rescale
-// check of tile j:
-//   block A: S^T(j+1) = K(j+1) Q^T (16 MFMAs)  beside  P(j) = 2^(c s - c m),
-//            its row sum and bf16 packing
-//   block B: O^T += V^T(j) P^T(j) (16 MFMAs)    beside  the row maximum of
-//            tile j+1 (masked where needed)
-// K and V have separate double buffers: block A reads K(j+1) and block B
-// V(j), so both stay resident for one iteration while K(j+2) and V(j+1)
-// load into the other halves.  The arithmetic per row is the same as in
-// prefill_bf16_kernel (same products, same order), only interleaved.
+// separate waves on a SIMD do not achieve.  Per tile j:
+//   block A: S^T(j+1) = K(j+1) Q^T (16 MFMAs)  beside  P(j) = 2^(c s - c m)
+//            against the running maximum, its row-sum parts and bf16 packing
+//   then the quick lazy-rescale test of tile j (as in pf_tile_step): only
+//            when a row-sum part exceeds 2^7 is tile j's maximum formed, the
+//            running maximum moved if it grew past 2^8 in weight, and P(j)
+//            formed again
+//   block B: O^T += V^T(j) P^T(j) (16 MFMAs)    beside  the masking of tile
+//            j+1 where needed
+// The first maximum is taken in the prologue, from tile 0.  K and V have
+// separate double buffers: block A reads K(j+1) and block B V(j), so both
+// stay resident for one iteration while K(j+2) and V(j+1) load into the other
+// halves.  The arithmetic per row is the same as in prefill_bf16_kernel (same
+// products, same order, the same rescale decisions), only interleaved.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -705,9 +709,9 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     };
 
     f32x16 sa[2], sb[2];
-    float mxa = kNegInf, mxb = kNegInf;
 
-    // Prologue: K(0), K(1), V(0) resident; scores and maximum of tile 0.
+    // Prologue: K(0), K(1), V(0) resident; scores of tile 0 and the first
+    // running maximum.
     load_k(0, kbuf0);
     if (n_kt > 1) load_k(1, kbuf1);
     load_v(0, vbuf0);
@@ -715,18 +719,29 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     __syncthreads();
     if (my_kt > 0) {
         pp.scores(kbuf0, sa);
-        mxa = tile_mask(0) ? pp.template rowmax<true>(sa, 0) : pp.template rowmax<false>(sa, 0);
+        if (tile_mask(0)) pp.template mask<true>(sa, 0);
+        pp.rescale(pp.rowmax_masked(sa));    // the first maximum (always a rescale)
     }
     __syncthreads();     // every wave's reads of K(0) precede the load into its buffer
 
     // Iteration j: K(j+1) in kn, V(j) in vc; loads of K(j+2) into kd and
     // V(j+1) into vd (their previous tiles were last read in iteration j-1).
     auto iter = [&](int j, const uint16_t* kn, const uint16_t* vc, uint16_t* kd, uint16_t* vd,
-                    f32x16 (&scur)[2], f32x16 (&snxt)[2], float& mcur, float& mnxt) {
+                    f32x16 (&scur)[2], f32x16 (&snxt)[2]) {
         if (j + 2 < n_kt) load_k(j + 2, kd);
         if (j + 1 < n_kt) load_v(j + 1, vd);
+        // Tile j's weights were taken against the running maximum (row-sum
+        // parts lsum); the full lazy-rescale test, from tile j's maximum, and
+        // the weights again only when a part exceeds 2^7 or some row has no
+        // maximum yet (as in pf_tile_step).
+        auto settle = [&](bf16x8 (&pb)[4], float lsum) {
+            if (__builtin_amdgcn_ballot_w64(m_run == kNegInf || !(lsum <= kLazyCheck)) != 0) {
+                pp.rescale(pp.rowmax_masked(scur));
+                lsum = pp.probs_part(scur, pb);
+            }
+            l_run += lsum;
+        };
         if (j + 1 < my_kt) {
-            pp.rescale(mcur);
             const int k1 = (j + 1) * PF_BN;
             // One straight-line path per mask case of tile j+1, so that each
             // block is a single scheduling region.
@@ -735,13 +750,15 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                 bf16x8 pb[4];
                 // block A
                 pp.scores(kn, snxt);
-                pp.probs(scur, pb);
+                const float lsum = pp.probs_part(scur, pb);
                 pf_interleave<2 * KS, 7, 6, 1>();
+                __builtin_amdgcn_sched_barrier(0);
+                settle(pb, lsum);
                 __builtin_amdgcn_sched_barrier(0);
                 // block B
                 pp.pv(vc, pb);
-                mnxt = pp.template rowmax<MASK>(snxt, k1);
-                pf_interleave<16, MASK ? 6 : 2, 12, 2>();
+                pp.template mask<MASK>(snxt, k1);
+                pf_interleave<16, MASK ? 4 : 0, 12, 2>();
                 __builtin_amdgcn_sched_barrier(0);
             };
             if (tile_mask(j + 1))
@@ -749,17 +766,16 @@ prefill_sp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             else
                 body(std::false_type{});
         } else if (j < my_kt) {
-            pp.rescale(mcur);
             bf16x8 pb[4];
-            pp.probs(scur, pb);
+            settle(pb, pp.probs_part(scur, pb));
             pp.pv(vc, pb);
         }
         __builtin_amdgcn_s_waitcnt(0);     // K(j+2), V(j+1) in LDS
         __syncthreads();
     };
     for (int j = 0; j < n_kt; j += 2) {
-        iter(j, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb, mxa, mxb);
-        if (j + 1 < n_kt) iter(j + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa, mxb, mxa);
+        iter(j, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+        if (j + 1 < n_kt) iter(j + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
     }
 
     // Epilogue: o = u / l, lse = m + ln l (natural log).

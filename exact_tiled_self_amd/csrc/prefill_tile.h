@@ -302,22 +302,44 @@ struct PfPipe {
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qf[ks], sacc[kb], 0, 0, 0);
         }
     }
-    // Row maximum of one tile of keys k0 .., masked to -inf where not allowed.
+    // Mask only (keys of tile k0 .. not allowed -> -inf).
     template <bool MASK>
-    __device__ __forceinline__ float rowmax(f32x16 (&sacc)[2], int k0) const {
-        float mx = kNegInf;
+    __device__ __forceinline__ void mask(f32x16 (&sacc)[2], int k0) const {
+        if (MASK) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (MASK) {
+                for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                     const bool ok = key < kend && (!CAUSAL || key <= mypos);
                     sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
                 }
-                mx = fmaxf(mx, sacc[kb][r]);
-            }
+        }
+    }
+    // Row maximum of an already masked tile.
+    __device__ __forceinline__ float rowmax_masked(const f32x16 (&sacc)[2]) const {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         return max_halves(mx);
+    }
+    // P = 2^(c s - c m) in bf16 and this lane's part of the row sum (not yet
+    // added to l).  Masked scores are -inf and give exactly 0 only for c > 0:
+    // callers send c = 0 elsewhere.
+    __device__ __forceinline__ float probs_part(const f32x16 (&sacc)[2], bf16x8 (&pb)[4]) const {
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        float lsum = 0.f;
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = fast_exp2(fmaf(sacc[c16 >> 1][(c16 & 1) * 8 + i], c, -mc));
+                lsum += p;
+                pb[c16][i] = (__bf16)p;
+            }
+        return lsum;
     }
     // Lazy rescale (as in pf_tile_step): only when some row's maximum grew by
     // more than 2^kLazyLog2, or on the first tile.
@@ -333,21 +355,6 @@ struct PfPipe {
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
             m_run = m_new;
         }
-    }
-    // P = 2^(c s - c m), row sum, bf16.  Masked scores are -inf and give
-    // exactly 0 only for c > 0: callers send c = 0 elsewhere.
-    __device__ __forceinline__ void probs(const f32x16 (&sacc)[2], bf16x8 (&pb)[4]) const {
-        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-        float lsum = 0.f;
-#pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = fast_exp2(fmaf(sacc[c16 >> 1][(c16 & 1) * 8 + i], c, -mc));
-                lsum += p;
-                pb[c16][i] = (__bf16)p;
-            }
-        l_run += lsum;
     }
     // O^T += V^T P^T of one tile (V^T operands one key block ahead).
     __device__ __forceinline__ void pv(const uint16_t* Vb, const bf16x8 (&pb)[4]) const {
