@@ -204,8 +204,8 @@ __device__ __forceinline__ void pf_tile_step(const uint16_t* Ks, const uint16_t*
 
     // Once every row has a running maximum, the weights are taken against it
     // directly.  A lane's part of a row sum bounds each of its weights, so
-    // when no part exceeds 2^kLazyCheckLog2 no score rose above the running
-    // maximum by 2^kLazyCheckLog2 in weight, fewer than the 2^kLazyLog2 that
+    // when no part exceeds kLazyCheck (2^7) no score rose above the running
+    // maximum by more than 2^7 in weight, less than the 2^kLazyLog2 that
     // would move it: the tile keeps the maximum, exactly as the full test
     // below decides.  Otherwise (rare after the first tile: a part that
     // large) the scores are computed again and take the full test.
