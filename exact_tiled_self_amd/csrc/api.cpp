@@ -162,11 +162,12 @@ attn_status check_decode_args(const void* q, const void* k_cache, const void* v_
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d is not supported (64 or 128)", d);
     if (block_size != attn::kDecodeBlock)
         return fail(ATTN_ERR_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
-    if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
     if ((long long)max_blocks * block_size >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "max_blocks too large");
     if ((long long)num_blocks * Hkv * block_size * d >= (1LL << 40))
         return fail(ATTN_ERR_UNSUPPORTED, "KV pool too large");
-    if ((long long)S * Hkv * max_blocks >= (1LL << 31) || S > 65535 || Hkv > 65535)
+    // (pairs of sequence and virtual kv head: at most 16 query heads each)
+    const long long hv = (long long)Hkv * attn::decode_groups(Hq / Hkv);
+    if ((long long)S * hv * max_blocks >= (1LL << 31) || S > 65535 || Hkv > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "too many sequences or blocks for one launch");
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
         return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");

@@ -28,7 +28,9 @@
 // length and blocks with an out-of-range table entry read as zeros without
 // a branch; scores of such slots are excluded before any arithmetic.  The G
 // query heads that share the kv head (grouped-query attention) form the rows
-// of the score tile, so both products run on MFMA:
+// of the score tile, so both products run on MFMA (more than 16 are split
+// into equal groups of at most 16, each handled as a kv head of its own that
+// reads the same K/V blocks):
 //   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (l16, grp) holds key l16's
 //     dims D/4*grp .. D/4*grp + D/4 - 1 (one contiguous run per lane; Q uses
 //     the same dim order), and gets back the scores of keys 4grp..4grp+3 for
@@ -114,6 +116,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ ctx_lens, int32_t* __restrict__ recs,
                     float* __restrict__ slots, uint16_t* __restrict__ o, float* __restrict__ lse,
                     int S, int Hq, int Hkv, int max_blocks, int num_blocks, float c, int negate) {
+    // (sequence, virtual kv head) pairs: the G query heads of kv head gp in
+    // NG groups of at most GV rows; virtual head v = gp * NG + group
+    const int G = Hq / Hkv, NG = decode_groups(G), GV = decode_group_rows(G), HV = Hkv * NG;
     constexpr int KS = D / 32;     // MFMA k-steps over the head dim
     constexpr int DPL = D / 16;    // output tiles; V dims per lane per key
     constexpr int QW = D / 4;      // dims per lane group in the score product
@@ -121,9 +126,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
     const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = Hq / Hkv, cap = max_blocks * kDecodeBlock;
-    const int mlp = decode_ml_pad(G);
-    const size_t sf = decode_slot_floats(G, D);
+    const int cap = max_blocks * kDecodeBlock;
+    const int mlp = decode_ml_pad(GV);
+    const size_t sf = decode_slot_floats(GV, D);
 
     // Total block count over the sequences.
     int n_first = 0, tot = 0;
@@ -135,12 +140,12 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     tot = __builtin_amdgcn_readfirstlane(tot);
     // Units are dealt to W = min(waves launched, U) waves, so that every
     // wave in [0, W) has at least one unit (the merge relies on it).
-    const long long U = (long long)tot * Hkv;
+    const long long U = (long long)tot * HV;
     const int W = (int)min((long long)gridDim.x * 4, U);
     if (w >= W) return;
     const long long u0 = (long long)w * U / W, u1 = (long long)(w + 1) * U / W;
 
-    // The sequence holding unit u0 (unit of (s, g, b) = Hkv*P_s + g*n_s + b,
+    // The sequence holding unit u0 (unit of (s, g, b) = HV*P_s + g*n_s + b,
     // P_s = blocks of the sequences before s).
     int s = 0, Ps = 0, ns = 0;
     {
@@ -148,7 +153,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int s0 = 0; s0 < S; s0 += 64) {
             const int n = (s0 == 0) ? n_first : ((s0 + lane < S) ? nblocks_of(ctx_lens[s0 + lane], cap) : 0);
             const int incl = wave_incl_scan(n, lane);
-            const long long lo = (long long)Hkv * (P + incl - n), hi = (long long)Hkv * (P + incl);
+            const long long lo = (long long)HV * (P + incl - n), hi = (long long)HV * (P + incl);
             const uint64_t hit = __builtin_amdgcn_ballot_w64(u0 >= lo && u0 < hi);
             if (hit) {
                 const int j = (int)__builtin_ctzll(hit);
@@ -166,23 +171,26 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     long long u = u0;
     while (true) {
         // ---- one piece: blocks [b0, b1) of pair (s, g) ----
-        const long long base = (long long)Hkv * Ps;
+        const long long base = (long long)HV * Ps;
         const int r0 = (int)(u - base);
-        const int g = r0 / ns, b0 = r0 - g * ns;
+        const int g = r0 / ns, b0 = r0 - g * ns;       // g: virtual kv head
         const long long pbeg = base + (long long)g * ns, pend = pbeg + ns;
         const long long send = pend < u1 ? pend : u1;
         const int b1 = b0 + (int)(send - u), nb = b1 - b0;
-        const int p = s * Hkv + g;
+        const int p = s * HV + g;
+        const int gp = g / NG, grp_i = g - gp * NG;    // physical kv head, group
+        const int gr = min(GV, G - grp_i * GV);        // query heads (rows) of this group
+        const int h0 = gp * G + grp_i * GV;            // its first query head
         const int ctx_raw = ctx_lens[s];
         const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
         const bool ctx_bad = ctx_raw < 0 || ctx_raw > cap;
 
-        // Q operand (B of S^T = K Q^T): query row l16 (head g*G + l16 when l16 < G).
+        // Q operand (B of S^T = K Q^T): query row l16 (head h0 + l16 when l16 < gr).
         bf16x8 qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 wq = {0u, 0u, 0u, 0u};
-            if (l16 < G) wq = ld16(q + ((size_t)s * Hq + g * G + l16) * D + QW * grp + 8 * ks);
+            if (l16 < gr) wq = ld16(q + ((size_t)s * Hq + h0 + l16) * D + QW * grp + 8 * ks);
             if (negate) wq = neg_bf16x8(wq);
             qf[ks] = __builtin_bit_cast(bf16x8, wq);
         }
@@ -205,7 +213,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 bad = bad || !ok;
                 const int nv = min(kDecodeBlock, ctx - kDecodeBlock * (b0 + cb + i));
                 bytes = ok ? nv * D * 2 : 0;
-                off = ((size_t)(ok ? e : 0) * Hkv + g) * (size_t)(kDecodeBlock * D);
+                off = ((size_t)(ok ? e : 0) * Hkv + gp) * (size_t)(kDecodeBlock * D);
             }
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + off, (uint32_t)bytes);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + off, (uint32_t)bytes);
@@ -306,8 +314,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             // the whole pair: final output
             const bool nan_out = bad || ctx_bad;
             const float inv = nan_out ? nanv : 1.f / l_run;
-            if (l16 < G) {
-                uint16_t* orow = o + ((size_t)s * Hq + g * G + l16) * D + QW * grp;
+            if (l16 < gr) {
+                uint16_t* orow = o + ((size_t)s * Hq + h0 + l16) * D + QW * grp;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     if constexpr (DPL == 8) {
@@ -325,14 +333,14 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     }
                 }
                 if (lse != nullptr && grp == 0)
-                    lse[(size_t)s * Hq + g * G + l16] = nan_out ? nanv : (m_run * c + log2f(l_run)) * kLn2;
+                    lse[(size_t)s * Hq + h0 + l16] = nan_out ? nanv : (m_run * c + log2f(l_run)) * kLn2;
             }
         } else {
             float* slot = slots + (size_t)(w + p) * sf;
-            if (l16 < G) {
+            if (l16 < gr) {
                 if (grp == 0) {
                     slot[l16] = m_run;
-                    slot[G + l16] = bad ? nanv : l_run;
+                    slot[GV + l16] = bad ? nanv : l_run;
                 }
                 float* ud = slot + mlp + (size_t)l16 * D + QW * grp;
 #pragma unroll
@@ -347,7 +355,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         // ---- next piece ----
         u = send;
         if (u >= u1) break;
-        if (g + 1 == Hkv) {
+        if (g + 1 == HV) {
             Ps += ns;
             do {
                 ++s;
@@ -373,18 +381,22 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
     constexpr int NQ = D / 4;     // 4-dim groups per row
     constexpr int BATCH = 16;
     const int p = blockIdx.x, lane = threadIdx.x;
-    const int s = p / Hkv, g = p - s * Hkv, G = Hq / Hkv;
+    // pair p = (sequence, virtual kv head), as in the split kernel
+    const int G = Hq / Hkv, NG = decode_groups(G), GV = decode_group_rows(G), HV = Hkv * NG;
+    const int s = p / HV, g = p - s * HV;
+    const int gp = g / NG, grp_i = g - gp * NG;
+    const int gr = min(GV, G - grp_i * GV), h0 = gp * G + grp_i * GV;
     const int e = blockIdx.y * 64 + lane;          // element: row e / NQ, dims 4*(e % NQ)..
     const int row = e / NQ, d4 = e - row * NQ;
-    const bool act = row < G;
+    const bool act = row < gr;
     const int cap = max_blocks * kDecodeBlock;
     // the record is read before the length check so both loads are in flight together
     const int wf = recs[2 * p], wl = recs[2 * p + 1];
     const int ctx_raw = ctx_lens[s];
     const bool bad = ctx_raw < 0 || ctx_raw > cap;
     const float nanv = __builtin_nanf("");
-    uint16_t* orow = o + ((size_t)s * Hq + g * G + row) * D + 4 * d4;
-    float* lse_out = (lse != nullptr && act && d4 == 0) ? lse + (size_t)s * Hq + g * G + row : nullptr;
+    uint16_t* orow = o + ((size_t)s * Hq + h0 + row) * D + 4 * d4;
+    float* lse_out = (lse != nullptr && act && d4 == 0) ? lse + (size_t)s * Hq + h0 + row : nullptr;
     if (nblocks_of(ctx_raw, cap) == 0) {
         if (act) {
             const uint32_t z = bad ? 0x7fc07fc0u : 0u;
@@ -395,8 +407,8 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
     }
     if (wf == wl || !act) return;
     const int nk = wl - wf + 1;
-    const size_t sf = decode_slot_floats(G, D);
-    const int mlp = decode_ml_pad(G);
+    const size_t sf = decode_slot_floats(GV, D);
+    const int mlp = decode_ml_pad(GV);
     const float* s0 = slots + (size_t)(wf + p) * sf;
 
     float M = kNegInf, L = 0.f;
@@ -409,7 +421,7 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
             const int k = min(k0 + j, nk - 1);
             const float* sl = s0 + (size_t)k * sf;
             mk[j] = sl[row];
-            lk[j] = sl[G + row];
+            lk[j] = sl[GV + row];
             uk[j] = *reinterpret_cast<const f32x4*>(sl + mlp + (size_t)row * D + 4 * d4);
         }
 #pragma unroll
@@ -447,10 +459,11 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
         const int v = atoi(env);
         if (v >= 4 && v <= kDecodeWaves) waves = v / 4 * 4;
     }
-    const long long units_max = (long long)a.S * a.Hkv * a.max_blocks;
+    const int G = a.Hq / a.Hkv, HV = a.Hkv * decode_groups(G);   // virtual kv heads
+    const long long units_max = (long long)a.S * HV * a.max_blocks;
     if (units_max < waves) waves = (int)((units_max + 3) / 4 * 4);
     int32_t* recs = reinterpret_cast<int32_t*>(a.workspace);
-    float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + decode_rec_bytes(a.S, a.Hkv));
+    float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + decode_rec_bytes(a.S, HV));
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(waves / 4)), dim3(DS_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, recs, slots,
@@ -458,8 +471,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        a.c, a.negate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int elems = (a.Hq / a.Hkv) * (D / 4);
-    const dim3 g2((unsigned)(a.S * a.Hkv), (unsigned)((elems + 63) / 64));
+    const int elems = decode_group_rows(G) * (D / 4);
+    const dim3 g2((unsigned)(a.S * HV), (unsigned)((elems + 63) / 64));
     hipLaunchKernelGGL((decode_merge_kernel<D>), g2, dim3(64), 0, stream, recs, slots, a.ctx_lens,
                        static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.max_blocks, a.c);
     return hipGetLastError();

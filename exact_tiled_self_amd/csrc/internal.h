@@ -49,11 +49,21 @@ inline size_t decode_rec_bytes(int S, int Hkv) {
 }
 __host__ __device__ inline int decode_ml_pad(int G) { return (2 * G + 3) & ~3; }
 __host__ __device__ inline size_t decode_slot_floats(int G, int d) { return (size_t)decode_ml_pad(G) + (size_t)G * d; }
+// The G query heads of a kv head are the rows of one 16-row score tile; more
+// than 16 are split into decode_groups(G) groups of at most
+// decode_group_rows(G) heads, each a "virtual" kv head of its own (its own
+// units, partial states and records; its K/V blocks read once per group).
+__host__ __device__ inline int decode_groups(int G) { return (G + 15) / 16; }
+__host__ __device__ inline int decode_group_rows(int G) { return (G + decode_groups(G) - 1) / decode_groups(G); }
 // Upper bound over every Hkv dividing Hq (the size query does not take Hkv).
+// With n = decode_groups(G) virtual heads per kv head of r rows each,
+// n * r <= G + n - 1 <= G + G / 16, so the rows of all pairs' slots are at
+// most S*Hq + S*Hq/16, and the waves' slots at most 2048 rows of <= Hq.
 inline size_t decode_workspace_bound(int S, int Hq, int d) {
     const size_t rec = (((size_t)S * Hq * 2 * sizeof(int32_t)) + 255) & ~(size_t)255;
-    const size_t slots_times_g = (size_t)kDecodeWaves * Hq + (size_t)S * Hq;   // >= (W + S*Hkv) * G
-    const size_t slots = (size_t)kDecodeWaves + (size_t)S * Hq;                // >= W + S*Hkv
+    const size_t sq = (size_t)S * Hq;
+    const size_t slots_times_g = (size_t)kDecodeWaves * Hq + sq + (sq + 15) / 16;   // >= (W + S*Hkv') * G'
+    const size_t slots = (size_t)kDecodeWaves + sq;                                  // >= W + S*Hkv'
     return rec + (slots_times_g * (size_t)(d + 2) + slots * 3) * sizeof(float);
 }
 
@@ -77,8 +87,9 @@ hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 // above bounds it over every Hkv instead).
 inline size_t decode_workspace_exact(int S, int Hq, int Hkv, int d) {
     const int G = Hq / Hkv;
-    return decode_rec_bytes(S, Hkv) +
-           ((size_t)kDecodeWaves + (size_t)S * Hkv) * decode_slot_floats(G, d) * sizeof(float);
+    const int hv = Hkv * decode_groups(G);   // virtual kv heads
+    return decode_rec_bytes(S, hv) +
+           ((size_t)kDecodeWaves + (size_t)S * hv) * decode_slot_floats(decode_group_rows(G), d) * sizeof(float);
 }
 
 // The same decode with its partial states in the library's own per-device

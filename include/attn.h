@@ -99,9 +99,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  * attn_paged_decode needs for these sizes (0 on invalid sizes).  The
  * workspace holds, per (sequence, kv head) pair, the first and last wave that
  * worked on it, and the fp32 partial states (m, l, u) that waves covering
- * only part of a pair leave for the merge.  The size is a bound that holds
+ * only part of a pair leave for the merge (with more than 16 query heads per
+ * kv head, per group of at most 16 of them).  The size is a bound that holds
  * for every Hkv dividing Hq: round_up(8*S*Hq, 256)
- * + 4*((2048 + S)*Hq*(d + 2) + 3*(2048 + S*Hq)) bytes.
+ * + 4*((2048*Hq + S*Hq + ceil(S*Hq/16))*(d + 2) + 3*(2048 + S*Hq)) bytes.
  */
 size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, int block_size);
 
@@ -128,8 +129,11 @@ size_t attn_paged_decode_workspace_size(int S, int Hq, int d, int max_blocks, in
  *                   are ignored.  Calls that share a workspace must be
  *                   ordered on one stream.
  *
- * Supported: dtype BF16; d = 64 or 128; block_size = 16; Hq % Hkv == 0
- * with Hq / Hkv <= 16; S, max_blocks, num_blocks >= 1.
+ * Supported: dtype BF16; d = 64 or 128; block_size = 16; Hq % Hkv == 0;
+ * S, max_blocks, num_blocks >= 1; S * n * Hkv * max_blocks < 2^31 with n as
+ * below.  The G = Hq / Hkv query heads of a kv head share each K/V block
+ * read; more than 16 are split into n = ceil(G / 16) groups of at most
+ * ceil(G / n) heads, and each group reads the kv head's blocks once.
  *
  * Device-resident values cannot be checked before launch.  A ctx_lens entry
  * outside [0, max_blocks * block_size] or a needed block_table entry outside
@@ -155,9 +159,9 @@ attn_status attn_paged_decode(const void* q, const void* k_cache, const void* v_
  * ATTN_DECODE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library
  * runs on holds until the process ends.  A call whose partial states would
  * not fit, i.e. when
- *     256-byte-rounded(8 * S * Hkv)
- *       + 4 * (2048 + S * Hkv) * (round4(2 * G) + G * d) > that size
- * with G = Hq / Hkv, returns ATTN_ERR_UNSUPPORTED before anything is
+ *     256-byte-rounded(8 * S * H) + 4 * (2048 + S * H) * (round4(2 * r) + r * d)
+ * exceeds that size, with G = Hq / Hkv, n = ceil(G / 16), H = n * Hkv and
+ * r = ceil(G / n), returns ATTN_ERR_UNSUPPORTED before anything is
  * enqueued (S * Hkv up to about 8700 fits at G = 6, d = 128; about 1900 at
  * G = 16).  Nothing is allocated, freed or memset.  Every call on one GPU
  * shares that GPU's array, so calls that may run at the same time on one

@@ -97,7 +97,10 @@ def dec(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A + 2
     (dict(o=0), INVALID), (dict(S=0), INVALID), (dict(max_blocks=0), INVALID),
     (dict(num_blocks=0), INVALID), (dict(Hq=12, Hkv=5), INVALID), (dict(scale=math.inf), INVALID),
     (dict(dtype=F32), UNSUPPORTED), (dict(d=80), UNSUPPORTED), (dict(bs=32), UNSUPPORTED),
-    (dict(Hq=34, Hkv=2), UNSUPPORTED), (dict(ws=0), INVALID), (dict(ws_bytes=16), INVALID),
+    (dict(ws=0), INVALID), (dict(ws_bytes=16), INVALID),
+    # 32 query heads per kv head run as two groups of 16: twice the units
+    # (17 * 2 * (2^26 - 1) >= 2^31, while 17 * (2^26 - 1) alone would fit)
+    (dict(S=17, Hq=32, Hkv=1, max_blocks=(1 << 26) - 1), UNSUPPORTED),
     (dict(q=A + 4), INVALID), (dict(table=A + 192 * MB + 2), INVALID), (dict(ws=A + 256 * MB + 8), INVALID),
     (dict(o=A + 64 * MB), INVALID), (dict(ws=A + 200 * MB), INVALID),
 ])
@@ -123,6 +126,8 @@ def dec_na(lib, q=A, kc=A + 64 * MB, vc=A + 128 * MB, table=A + 192 * MB, ctx=A 
     # partial states of 2048 + S * Hkv pieces beyond the 32 MiB static array
     (dict(S=9000, Hq=12, Hkv=2, max_blocks=1, o=A + 512 * MB, lse=A + 1024 * MB), UNSUPPORTED),
     (dict(S=3000, Hq=16, Hkv=1, max_blocks=1, o=A + 512 * MB, lse=A + 1024 * MB), UNSUPPORTED),
+    # 32 heads per kv head: two groups, so 1000 sequences no longer fit
+    (dict(S=1000, Hq=32, Hkv=1, max_blocks=1, o=A + 512 * MB, lse=A + 1024 * MB), UNSUPPORTED),
 ])
 def test_decode_noalloc_rejects_before_any_launch(lib, kw, status):
     assert dec_na(lib, **kw) == status
@@ -134,24 +139,30 @@ def test_decode_noalloc_capacity_bound():
     64-sequence workload (12/2 heads, d = 128) fits, with room to spare."""
     def need(S, Hq, Hkv, d):
         G = Hq // Hkv
-        rec = (8 * S * Hkv + 255) // 256 * 256
-        return rec + 4 * (2048 + S * Hkv) * (((2 * G + 3) // 4 * 4) + G * d)
+        n = -(-G // 16)
+        H, r = n * Hkv, -(-G // n)
+        rec = (8 * S * H + 255) // 256 * 256
+        return rec + 4 * (2048 + S * H) * (((2 * r + 3) // 4 * 4) + r * d)
     cap = _lib.DECODE_NOALLOC_SCRATCH_BYTES
     assert need(64, 12, 2, 128) < cap // 4
     assert need(4300, 12, 2, 128) <= cap < need(4400, 12, 2, 128)
     assert need(1900, 16, 1, 128) <= cap < need(2000, 16, 1, 128)
     assert need(9000, 12, 2, 128) > cap and need(3000, 16, 1, 128) > cap
+    # 32 heads per kv head: two groups of 16, so half the sequences fit
+    assert need(900, 32, 1, 128) <= cap < need(1000, 32, 1, 128)
 
 
 def test_workspace_size(lib):
     # documented bound: 8*S*Hq bytes of pair records rounded up to 256, then
-    # fp32 partial states for up to 2048 + S*Hq wave pieces
+    # fp32 partial states for up to 2048 + S*Hq wave pieces, whose rows number
+    # at most 2048*Hq + S*Hq + ceil(S*Hq/16) (groups of at most 16 heads)
     def expect(S, Hq, d):
         rec = (8 * S * Hq + 255) // 256 * 256
-        return rec + 4 * ((2048 + S) * Hq * (d + 2) + 3 * (2048 + S * Hq))
+        return rec + 4 * ((2048 * Hq + S * Hq + -(-S * Hq // 16)) * (d + 2) + 3 * (2048 + S * Hq))
     assert lib.attn_paged_decode_workspace_size(64, 12, 128, 512, 16) == expect(64, 12, 128)
     assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 16) == expect(1, 1, 64)
     assert lib.attn_paged_decode_workspace_size(3, 8, 64, 7, 16) == expect(3, 8, 64)
+    assert lib.attn_paged_decode_workspace_size(5, 71, 128, 9, 16) == expect(5, 71, 128)
     assert lib.attn_paged_decode_workspace_size(1, 1, 64, 1, 32) == 0
     assert lib.attn_paged_decode_workspace_size(0, 1, 64, 1, 16) == 0
 

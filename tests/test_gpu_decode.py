@@ -2,8 +2,9 @@
 64-sequence workload, ragged lengths, NaN poison in every slot that must not
 be read, a spike key located through the block table, an identity table
 against dense attention, empty contexts, bad device-resident lengths and
-table entries, many sequences, the wave count forced down (long pieces,
-several pieces per wave, wide merges) and determinism."""
+table entries, many sequences, more than 16 query heads per kv head, the
+wave count forced down (long pieces, several pieces per wave, wide merges)
+and determinism."""
 
 import math
 import os
@@ -213,6 +214,35 @@ def test_many_short_sequences():
     p = paged_inputs(small_cfg(Hq=8, Hkv=2, d=64), S=200, ctx_lens=ctx.tolist(), poison=True,
                      max_blocks=3, seed=44)
     check(p, 0.125, "S=200 short")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(17, 1), (40, 2), (32, 1), (71, 1)])
+def test_more_than_16_heads_per_kv_head(d, Hq, Hkv):
+    """More than 16 query heads per kv head (multi-query models) run as groups
+    of at most 16 rows that each read the kv head's blocks: 17 heads as 9 + 8,
+    20 as 10 + 10, 32 as 16 + 16, 71 as four groups of 15 and one of 11."""
+    ctx = [1, 16, 17, 300, 0, 1000, 2000, 64]
+    p = paged_inputs(small_cfg(Hq, Hkv, d), S=len(ctx), ctx_lens=ctx, poison=True, extra_blocks=4,
+                     max_blocks=130, seed=Hq + d)
+    check(p, 1.0 / math.sqrt(d), f"groups d{d} {Hq}/{Hkv}")
+
+
+@pytest.mark.parametrize("waves", [4, 36])
+def test_head_groups_with_few_waves(monkeypatch, waves):
+    """Head groups with long pieces: a wave's units run across the groups of
+    a kv head, across kv heads and across sequences, and pairs are merged from
+    many waves."""
+    rng = np.random.default_rng(47)
+    ctx = rng.integers(0, 2500, 20)
+    ctx[[2, 9]] = 0
+    p = paged_inputs(small_cfg(48, 2, 128), S=20, ctx_lens=ctx.tolist(), poison=True, extra_blocks=4,
+                     max_blocks=160, seed=48)
+    monkeypatch.setenv("ATTN_DECODE_WAVES", str(waves))
+    o, lse = run_decode(p, 0.0884)
+    check(p, 0.0884, f"groups waves={waves}")
+    o2, lse2 = run_decode(p, 0.0884)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
 @pytest.mark.parametrize("waves", [4, 2048])
