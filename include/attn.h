@@ -55,7 +55,8 @@ typedef enum {
     ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, overlap,
                                    Hq % Hkv != 0, non-finite scale, small workspace */
     ATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented: head dim, dtype,
-                                   block size, group size, device architecture */
+                                   block size, sizes beyond one launch, device
+                                   architecture */
     ATTN_ERR_NO_DEVICE = 3,     /* no HIP device is current / visible */
     ATTN_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch */
 } attn_status;
