@@ -604,7 +604,7 @@ def main(argv=None):
                    "flushed_median_us": round(float(np.median(fl_ms)) * 1e3, 2),
                    "flushed_GBps": round(db / (fl_avg * 1e-3) / 1e9, 1),
                    "graph_replay_median_us": round(float(np.median(g_ms)) * 1e3, 2),
-                   "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
+                   "kernels": "decode_split_kernel<128, 0> + decode_merge_kernel<128, 0>",
                    "traffic": profiled_traffic("paged_decode_bf16_d128_s64",
                                                ["decode_paged.hip", "common.h", "internal.h"])},
         "chunked_prefill": {
@@ -656,7 +656,7 @@ def main(argv=None):
     # sources changed since they were taken), and the consistency checks
     # between them and the event timings
     dec_prof = profile_figures("paged_decode_bf16_d128_s64", ["decode_paged.hip", "common.h", "internal.h"],
-                               "decode_split_kernel<128>")
+                               "decode_split_kernel<128, 0>")
     pre_prof = profile_figures("prefill_bf16_d128_causal_gqa_t8192",
                                ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"],
                                "prefill_sp_kernel<128, true>")

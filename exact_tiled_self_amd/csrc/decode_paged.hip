@@ -28,9 +28,7 @@
 // length and blocks with an out-of-range table entry read as zeros without
 // a branch; scores of such slots are excluded before any arithmetic.  The G
 // query heads that share the kv head (grouped-query attention) form the rows
-// of the score tile, so both products run on MFMA (more than 16 are split
-// into equal groups of at most 16, each handled as a kv head of its own that
-// reads the same K/V blocks):
+// of the score tile, so both products run on MFMA:
 //   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (l16, grp) holds key l16's
 //     dims D/4*grp .. D/4*grp + D/4 - 1 (one contiguous run per lane; Q uses
 //     the same dim order), and gets back the scores of keys 4grp..4grp+3 for
@@ -42,6 +40,14 @@
 //     packs key pairs with v_perm; tile j holds dims D/16*m + j.  The output
 //     comes back as one query row per lane with D/4 consecutive dims, so the
 //     rescale by e^(m - m') is lane-local.
+//
+// More than 16 query heads per kv head are split into equal groups of at
+// most 16.  Up to 4 groups, the waves of one workgroup form a team that
+// takes the kv head's units together, one group per wave, so that a block
+// the first wave reads is in the CU's caches for the others; beyond 4, each
+// group is a kv head of its own in the unit order.  Units are then dealt to
+// teams (a lone wave is a team of one), and the partial states and records
+// above are per (team, member).
 
 #include <stdlib.h>
 
@@ -103,13 +109,13 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
     return x;
 }
 
-// With U units dealt to W waves as [floor(wU/W), floor((w+1)U/W)), the wave
-// that covers unit u.
+// With U units dealt to W waves (or teams) as [floor(wU/W), floor((w+1)U/W)),
+// the one that covers unit u.
 __device__ __forceinline__ int wave_of_unit(long long u, long long U, int W) {
     return (int)(((u + 1) * (long long)W - 1) / U);
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ void __launch_bounds__(DS_THREADS)
 decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                     const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
@@ -117,15 +123,27 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float* __restrict__ slots, uint16_t* __restrict__ o, float* __restrict__ lse,
                     int S, int Hq, int Hkv, int max_blocks, int num_blocks, float c, int negate) {
     // (sequence, virtual kv head) pairs: the G query heads of kv head gp in
-    // NG groups of at most GV rows; virtual head v = gp * NG + group
-    const int G = Hq / Hkv, NG = decode_groups(G), GV = decode_group_rows(G), HV = Hkv * NG;
+    // NG groups of at most GV rows; virtual head v = gp * NG + group.  With
+    // NL = NG <= 4 groups, the NL waves of a team (one workgroup) take the
+    // same units of kv head gp, one group each, so that their reads of a
+    // block meet in the CU's caches; otherwise (NL = 1) every virtual head
+    // has units of its own.  HU: heads in the unit order.
+    // MODE (compile time): 0 one group (G <= 16), 1 groups without teams,
+    // 2 teams.
+    const int G = Hq / Hkv, NG = MODE ? decode_groups(G) : 1, GV = MODE ? decode_group_rows(G) : G;
+    const int HV = Hkv * NG, NL = MODE == 2 ? decode_team(G) : 1, HU = HV / NL;
     constexpr int KS = D / 32;     // MFMA k-steps over the head dim
     constexpr int DPL = D / 16;    // output tiles; V dims per lane per key
     constexpr int QW = D / 4;      // dims per lane group in the score product
     constexpr int NB = DS_NBUF, LA = DS_NBUF - 1;
 
     const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
-    const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // team wt (4 / NL teams per workgroup), member jm; a wave past the last
+    // team of its workgroup (NL = 3) has nothing to do
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tpw = 4 / NL;
+    if (wv >= tpw * NL) return;
+    const int wt = blockIdx.x * tpw + wv / NL, jm = wv - (wv / NL) * NL;
     const int cap = max_blocks * kDecodeBlock;
     const int mlp = decode_ml_pad(GV);
     const size_t sf = decode_slot_floats(GV, D);
@@ -138,14 +156,14 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         tot += wave_sum_i(n);
     }
     tot = __builtin_amdgcn_readfirstlane(tot);
-    // Units are dealt to W = min(waves launched, U) waves, so that every
-    // wave in [0, W) has at least one unit (the merge relies on it).
-    const long long U = (long long)tot * HV;
-    const int W = (int)min((long long)gridDim.x * 4, U);
-    if (w >= W) return;
-    const long long u0 = (long long)w * U / W, u1 = (long long)(w + 1) * U / W;
+    // Units are dealt to W = min(teams launched, U) teams, so that every
+    // team in [0, W) has at least one unit (the merge relies on it).
+    const long long U = (long long)tot * HU;
+    const int W = (int)min((long long)gridDim.x * tpw, U);
+    if (wt >= W) return;
+    const long long u0 = (long long)wt * U / W, u1 = (long long)(wt + 1) * U / W;
 
-    // The sequence holding unit u0 (unit of (s, g, b) = HV*P_s + g*n_s + b,
+    // The sequence holding unit u0 (unit of (s, gu, b) = HU*P_s + gu*n_s + b,
     // P_s = blocks of the sequences before s).
     int s = 0, Ps = 0, ns = 0;
     {
@@ -153,7 +171,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int s0 = 0; s0 < S; s0 += 64) {
             const int n = (s0 == 0) ? n_first : ((s0 + lane < S) ? nblocks_of(ctx_lens[s0 + lane], cap) : 0);
             const int incl = wave_incl_scan(n, lane);
-            const long long lo = (long long)HV * (P + incl - n), hi = (long long)HV * (P + incl);
+            const long long lo = (long long)HU * (P + incl - n), hi = (long long)HU * (P + incl);
             const uint64_t hit = __builtin_amdgcn_ballot_w64(u0 >= lo && u0 < hi);
             if (hit) {
                 const int j = (int)__builtin_ctzll(hit);
@@ -171,12 +189,13 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     long long u = u0;
     while (true) {
         // ---- one piece: blocks [b0, b1) of pair (s, g) ----
-        const long long base = (long long)HV * Ps;
+        const long long base = (long long)HU * Ps;
         const int r0 = (int)(u - base);
-        const int g = r0 / ns, b0 = r0 - g * ns;       // g: virtual kv head
-        const long long pbeg = base + (long long)g * ns, pend = pbeg + ns;
+        const int gu = r0 / ns, b0 = r0 - gu * ns;     // gu: head of the unit order
+        const long long pbeg = base + (long long)gu * ns, pend = pbeg + ns;
         const long long send = pend < u1 ? pend : u1;
         const int b1 = b0 + (int)(send - u), nb = b1 - b0;
+        const int g = gu * NL + jm;                    // virtual kv head
         const int p = s * HV + g;
         const int gp = g / NG, grp_i = g - gp * NG;    // physical kv head, group
         const int gr = min(GV, G - grp_i * GV);        // query heads (rows) of this group
@@ -307,8 +326,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         l_run += xor_shfl(l_run, 16);
         l_run += xor_shfl(l_run, 32);
         if (b0 == 0 && lane == 0) {
-            recs[2 * p] = w;                                   // first wave of the pair
-            recs[2 * p + 1] = wave_of_unit(pend - 1, U, W);    // last wave of the pair
+            recs[2 * p] = wt;                                  // first team of the pair
+            recs[2 * p + 1] = wave_of_unit(pend - 1, U, W);    // last team of the pair
         }
         if (b0 == 0 && b1 == ns) {
             // the whole pair: final output
@@ -336,7 +355,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     lse[(size_t)s * Hq + h0 + l16] = nan_out ? nanv : (m_run * c + log2f(l_run)) * kLn2;
             }
         } else {
-            float* slot = slots + (size_t)(w + p) * sf;
+            // slot of (team, unit pair, member): teams visit the unit pairs
+            // in increasing order, so wt + (s * HU + gu) is unique per piece
+            float* slot = slots + ((size_t)(wt + s * HU + gu) * NL + jm) * sf;
             if (l16 < gr) {
                 if (grp == 0) {
                     slot[l16] = m_run;
@@ -355,7 +376,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         // ---- next piece ----
         u = send;
         if (u >= u1) break;
-        if (g + 1 == HV) {
+        if (gu + 1 == HU) {
             Ps += ns;
             do {
                 ++s;
@@ -366,14 +387,14 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 }
 
 // Merge: one wave per (pair, 64 (row, 4-dim) elements).  Each lane walks
-// the partial states that the waves wf..wl left for the pair, in wave order
+// the partial states that the teams wf..wl left for the pair, in team order
 // (deterministic), sixteen at a time with all their loads issued together,
 // and keeps a running merged state: when a part's m exceeds the running
 // maximum the running l and u are rescaled first, so every part enters with
-// the weight e^(m_k - M).  Pairs covered by one wave were finished by that
-// wave; empty sequences give o = 0 and lse = -inf (NaN for a length outside
+// the weight e^(m_k - M).  Pairs covered by one team were finished by it;
+// empty sequences give o = 0 and lse = -inf (NaN for a length outside
 // [0, max_blocks * 16]).
-template <int D>
+template <int D, int MODE>
 __global__ void __launch_bounds__(64)
 decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ slots,
                     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ o,
@@ -381,11 +402,15 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
     constexpr int NQ = D / 4;     // 4-dim groups per row
     constexpr int BATCH = 16;
     const int p = blockIdx.x, lane = threadIdx.x;
-    // pair p = (sequence, virtual kv head), as in the split kernel
-    const int G = Hq / Hkv, NG = decode_groups(G), GV = decode_group_rows(G), HV = Hkv * NG;
+    // pair p = (sequence, virtual kv head), as in the split kernel; its
+    // pieces were left by teams wf..wl, member jm, in the slots of unit pair
+    // pu = s * HU + gu
+    const int G = Hq / Hkv, NG = MODE ? decode_groups(G) : 1, GV = MODE ? decode_group_rows(G) : G;
+    const int HV = Hkv * NG, NL = MODE == 2 ? decode_team(G) : 1, HU = HV / NL;
     const int s = p / HV, g = p - s * HV;
     const int gp = g / NG, grp_i = g - gp * NG;
     const int gr = min(GV, G - grp_i * GV), h0 = gp * G + grp_i * GV;
+    const int gu = g / NL, jm = g - gu * NL;
     const int e = blockIdx.y * 64 + lane;          // element: row e / NQ, dims 4*(e % NQ)..
     const int row = e / NQ, d4 = e - row * NQ;
     const bool act = row < gr;
@@ -409,7 +434,8 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
     const int nk = wl - wf + 1;
     const size_t sf = decode_slot_floats(GV, D);
     const int mlp = decode_ml_pad(GV);
-    const float* s0 = slots + (size_t)(wf + p) * sf;
+    const float* s0 = slots + ((size_t)(wf + s * HU + gu) * NL + jm) * sf;
+    const size_t sstep = (size_t)NL * sf;     // the next team's slot of the pair
 
     float M = kNegInf, L = 0.f;
     f32x4 U = {0.f, 0.f, 0.f, 0.f};
@@ -419,7 +445,7 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             const int k = min(k0 + j, nk - 1);
-            const float* sl = s0 + (size_t)k * sf;
+            const float* sl = s0 + (size_t)k * sstep;
             mk[j] = sl[row];
             lk[j] = sl[GV + row];
             uk[j] = *reinterpret_cast<const f32x4*>(sl + mlp + (size_t)row * D + 4 * d4);
@@ -449,7 +475,7 @@ decode_merge_kernel(const int32_t* __restrict__ recs, const float* __restrict__ 
     }
 }
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     // ATTN_DECODE_WAVES (4..2048, a multiple of 4) sets the wave count, so
     // that tests can reach long pieces, many pieces per wave and wide merges
@@ -459,12 +485,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
         const int v = atoi(env);
         if (v >= 4 && v <= kDecodeWaves) waves = v / 4 * 4;
     }
-    const int G = a.Hq / a.Hkv, HV = a.Hkv * decode_groups(G);   // virtual kv heads
-    const long long units_max = (long long)a.S * HV * a.max_blocks;
-    if (units_max < waves) waves = (int)((units_max + 3) / 4 * 4);
+    // virtual kv heads, waves per team, teams per workgroup
+    const int G = a.Hq / a.Hkv, HV = a.Hkv * decode_groups(G), NL = MODE == 2 ? decode_team(G) : 1, tpw = 4 / NL;
+    const long long units_max = (long long)a.S * (HV / NL) * a.max_blocks;
+    if (units_max < (long long)(waves / 4) * tpw) waves = (int)((units_max + tpw - 1) / tpw * 4);
     int32_t* recs = reinterpret_cast<int32_t*>(a.workspace);
     float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + decode_rec_bytes(a.S, HV));
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(waves / 4)), dim3(DS_THREADS), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3((unsigned)(waves / 4)), dim3(DS_THREADS), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_table, a.ctx_lens, recs, slots,
                        static_cast<uint16_t*>(a.o), a.lse, a.S, a.Hq, a.Hkv, a.max_blocks, a.num_blocks,
@@ -473,7 +500,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int elems = decode_group_rows(G) * (D / 4);
     const dim3 g2((unsigned)(a.S * HV), (unsigned)((elems + 63) / 64));
-    hipLaunchKernelGGL((decode_merge_kernel<D>), g2, dim3(64), 0, stream, recs, slots, a.ctx_lens,
+    hipLaunchKernelGGL((decode_merge_kernel<D, MODE>), g2, dim3(64), 0, stream, recs, slots, a.ctx_lens,
                        static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.max_blocks, a.c);
     return hipGetLastError();
 }
@@ -481,7 +508,15 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_paged_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-    return a.d == 128 ? launch_decode_t<128>(a, stream) : launch_decode_t<64>(a, stream);
+    // one build per grouping (one group; groups without teams; teams), so
+    // that each carries only its own index arithmetic
+    const int G = a.Hq / a.Hkv;
+    const int mode = decode_groups(G) == 1 ? 0 : (decode_team(G) > 1 ? 2 : 1);
+    if (a.d == 128)
+        return mode == 0 ? launch_decode_t<128, 0>(a, stream)
+                         : (mode == 1 ? launch_decode_t<128, 1>(a, stream) : launch_decode_t<128, 2>(a, stream));
+    return mode == 0 ? launch_decode_t<64, 0>(a, stream)
+                     : (mode == 1 ? launch_decode_t<64, 1>(a, stream) : launch_decode_t<64, 2>(a, stream));
 }
 
 // The partial states of attn_paged_decode_noalloc: a device array owned by

@@ -55,6 +55,9 @@ __host__ __device__ inline size_t decode_slot_floats(int G, int d) { return (siz
 // units, partial states and records; its K/V blocks read once per group).
 __host__ __device__ inline int decode_groups(int G) { return (G + 15) / 16; }
 __host__ __device__ inline int decode_group_rows(int G) { return (G + decode_groups(G) - 1) / decode_groups(G); }
+// Waves that read the same blocks together, one group each: all the groups
+// when they fit in one 4-wave workgroup, else 1 (each group on its own).
+__host__ __device__ inline int decode_team(int G) { return decode_groups(G) <= 4 ? decode_groups(G) : 1; }
 // Upper bound over every Hkv dividing Hq (the size query does not take Hkv).
 // With n = decode_groups(G) virtual heads per kv head of r rows each,
 // n * r <= G + n - 1 <= G + G / 16, so the rows of all pairs' slots are at

@@ -217,11 +217,14 @@ def test_many_short_sequences():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("Hq,Hkv", [(17, 1), (40, 2), (32, 1), (71, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(17, 1), (40, 2), (32, 1), (48, 1), (64, 1), (71, 1)])
 def test_more_than_16_heads_per_kv_head(d, Hq, Hkv):
     """More than 16 query heads per kv head (multi-query models) run as groups
-    of at most 16 rows that each read the kv head's blocks: 17 heads as 9 + 8,
-    20 as 10 + 10, 32 as 16 + 16, 71 as four groups of 15 and one of 11."""
+    of at most 16 rows: 17 heads as 9 + 8, 20 as 10 + 10, 32 as 16 + 16 (teams
+    of two waves), 48 as three groups of 16 (teams of three, the fourth wave
+    of each workgroup idle), 64 as four of 16 (teams of four), 71 as four
+    groups of 15 and one of 11 (five groups: no teams, each group a kv head
+    of its own)."""
     ctx = [1, 16, 17, 300, 0, 1000, 2000, 64]
     p = paged_inputs(small_cfg(Hq, Hkv, d), S=len(ctx), ctx_lens=ctx, poison=True, extra_blocks=4,
                      max_blocks=130, seed=Hq + d)
@@ -229,18 +232,20 @@ def test_more_than_16_heads_per_kv_head(d, Hq, Hkv):
 
 
 @pytest.mark.parametrize("waves", [4, 36])
-def test_head_groups_with_few_waves(monkeypatch, waves):
-    """Head groups with long pieces: a wave's units run across the groups of
-    a kv head, across kv heads and across sequences, and pairs are merged from
-    many waves."""
+@pytest.mark.parametrize("Hq,Hkv", [(48, 2), (48, 1), (128, 2), (144, 2)])
+def test_head_groups_with_few_waves(monkeypatch, waves, Hq, Hkv):
+    """Head groups with long pieces: a team's (or, beyond four groups, a
+    wave's) units run across kv heads and sequences, and pairs are merged
+    from many teams: 24 heads per kv head in teams of two, 48 in teams of
+    three, 64 in teams of four, 72 as five groups without teams."""
     rng = np.random.default_rng(47)
     ctx = rng.integers(0, 2500, 20)
     ctx[[2, 9]] = 0
-    p = paged_inputs(small_cfg(48, 2, 128), S=20, ctx_lens=ctx.tolist(), poison=True, extra_blocks=4,
+    p = paged_inputs(small_cfg(Hq, Hkv, 128), S=20, ctx_lens=ctx.tolist(), poison=True, extra_blocks=4,
                      max_blocks=160, seed=48)
     monkeypatch.setenv("ATTN_DECODE_WAVES", str(waves))
     o, lse = run_decode(p, 0.0884)
-    check(p, 0.0884, f"groups waves={waves}")
+    check(p, 0.0884, f"groups {Hq}/{Hkv} waves={waves}")
     o2, lse2 = run_decode(p, 0.0884)
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 

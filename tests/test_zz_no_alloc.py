@@ -71,9 +71,10 @@ def test_noalloc_matches_workspace_call_twice():
 
 
 def test_noalloc_other_group_sizes():
-    """Other head groupings (up to 20 query heads per kv head, run as two
-    groups of 10) and d = 64 go through the same array."""
-    for Hq, Hkv, d in ((16, 1, 128), (8, 8, 64), (6, 3, 128), (40, 2, 128)):
+    """Other head groupings (up to 48 query heads per kv head, run as
+    groups of at most 16 by teams of waves) and d = 64 go through the same
+    array."""
+    for Hq, Hkv, d in ((16, 1, 128), (8, 8, 64), (6, 3, 128), (40, 2, 128), (48, 1, 64)):
         cfg = PagedConfig("g", S=1, Hq=Hq, Hkv=Hkv, d=d, block_size=16, ctx_lo=1, ctx_hi=1, max_blocks=1,
                           dtype="bf16", seed=0)
         ctx = [5, 700, 64, 1300]
