@@ -251,12 +251,14 @@ def test_head_groups_with_few_waves(monkeypatch, waves, Hq, Hkv):
 
 
 @pytest.mark.parametrize("waves", [4, 2048])
-def test_bad_device_inputs_give_nan(monkeypatch, waves):
+@pytest.mark.parametrize("Hq,Hkv", [(12, 2), (64, 2)])
+def test_bad_device_inputs_give_nan(monkeypatch, waves, Hq, Hkv):
     """Lengths outside [0, max_blocks*16] and needed table entries outside
     [0, num_blocks) make that sequence's outputs NaN, touch nothing out of
-    bounds, and leave the other sequences exact."""
+    bounds, and leave the other sequences exact (also with 32 query heads
+    per kv head, read by teams of two waves)."""
     ctx = [100, 300, 200, 50, 700, 33]
-    p = paged_inputs(small_cfg(), S=6, ctx_lens=ctx, poison=True, max_blocks=48, seed=45)
+    p = paged_inputs(small_cfg(Hq, Hkv), S=6, ctx_lens=ctx, poison=True, max_blocks=48, seed=45)
     ref_o, ref_l = oracle_decode(p, 0.0884)
     cap = 48 * 16
     p["ctx_lens"] = p["ctx_lens"].clone()
