@@ -2,7 +2,8 @@
 of dq, dk and dv on ragged shapes (one row, tile edges, several tiles and a
 ragged tail), causal and not, grouped and ungrouped heads, d = 64 and 128,
 scales 0, negative and default, and the full causal GQA 8192-token workload;
-plus determinism and the scale-0 closed form on the GPU.
+plus determinism, the scale-0 closed form on the GPU, and the autograd
+wrapper that joins attn_fwd and attn_bwd.
 
 Tolerance (derived in the design notes): every gradient element within
 2e-2 * max(1, max |reference| of that tensor) - the bf16 output rounding is
@@ -105,3 +106,30 @@ def test_deterministic():
     b = run(q, k, v, do, 0.0884, True)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_attention(causal):
+    """attention() under torch autograd: its output is attn_fwd's and the
+    gradients of a loss are attn_bwd's for that loss's upstream gradient, bit
+    for bit, and the oracle's within the tolerance.  The loss reads o
+    transposed, so the upstream gradient arrives as a non-contiguous view."""
+    from exact_tiled_self_amd import attention
+    B, Hq, Hkv, N, d = 1, 4, 2, 150, 64
+    q, k, v = dense_inputs(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=13)
+    w = _dout((B, Hq, d, N), 14)          # weights of the loss on o^T
+    qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
+    o = attention(qd, kd, vd, causal=causal)
+    loss = (o.transpose(2, 3).float() * w.to(DEV).float()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    o_ref, lse = attn_fwd(qd.detach(), kd.detach(), vd.detach(), causal=causal)
+    assert torch.equal(o.detach(), o_ref)
+    do = w.transpose(2, 3).contiguous()   # d loss / d o, already bf16 values
+    dq, dk, dv = attn_bwd(qd.detach(), kd.detach(), vd.detach(), o_ref, lse, do.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    for g, r in ((qd.grad, dq), (kd.grad, dk), (vd.grad, dv)):
+        assert g.dtype == torch.bfloat16 and torch.equal(g.view(torch.int16), r.view(torch.int16))
+    ref = OB.attention_bwd(f64(q), f64(k), f64(v), f64(do), 1.0 / math.sqrt(d), causal)
+    for g, r in zip((qd.grad, kd.grad, vd.grad), ref):
+        assert np.abs(f64(g.cpu()) - r).max() <= REL * max(1.0, float(np.abs(r).max()))
