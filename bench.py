@@ -630,7 +630,7 @@ def main(argv=None):
             "frac_mfma": round(bf / (bw_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "avg_us": round(bw_avg * 1e3, 2), "median_us": round(float(np.median(bw_ms)) * 1e3, 2),
             "min_us": round(min(bw_ms) * 1e3, 2), "flops": bf,
-            "kernels": "bwd_prep + bwd_dq + bwd_kv (dV pass) + bwd_kv (dK pass) + bwd_reduce",
+            "kernels": "bwd_prep + bwd_dq + bwd_kvf (dK and dV) + bwd_reduce",
             "traffic": profiled_traffic("backward_bf16_d128_causal_gqa_t8192",
                                         ["backward_bf16.hip", "prefill_tile.h", "common.h", "internal.h"])},
         "fusion": {

@@ -10,7 +10,7 @@
 //   dv_j = sum_i p_ij do_i,   dp_ij = <do_i, v_j>,   ds_ij = p_ij (dp_ij - D_i)
 //   dq_i = scale * sum_j ds_ij k_j,   dk_j = scale * sum_i ds_ij q_i
 //
-// Five kernels, none with atomics (results are deterministic):
+// Four kernels, none with atomics (results are deterministic):
 //   * bwd_prep: D_i from o and do (fp32), into the workspace.
 //   * bwd_dq: 4 waves x 32 query rows, key tiles of 32; per tile S^T = K Q^T
 //     and dP^T = V dO^T on MFMA (a lane owns one query row, so lse_i and D_i
@@ -18,17 +18,20 @@
 //     dS^T taken straight from the accumulators as the B operand.  K and V
 //     tiles go straight to LDS, row-major; K^T is read from the K tile with
 //     LDS transpose loads.  Two buffers, one loading while one computes.
-//   * bwd_kv (twice): 4 waves x 32 keys, query chunks of 32; a lane owns one
-//     key, its K (and V) rows stay in registers.  The dV pass computes
-//     S = Q K^T, P and dV^T += dO^T P; the dK pass S, dP = dO V^T,
-//     dS = P (dP - D) and dK^T += Q^T dS.  Q, dO, lse and D go straight to
-//     LDS in a ring of three chunks, last chunk first; dO^T and Q^T come
-//     from transpose loads.
-//   * bwd_reduce: with grouped K/V heads the two passes write one fp32
-//     dk, dv per query head into the workspace and this kernel sums each
-//     group in head order into the bf16 outputs.
+//   * bwd_kvf: 4 waves x 32 keys, query chunks of 32; a lane owns one key,
+//     its K and V rows stay in registers.  Per chunk S = Q K^T,
+//     dP = dO V^T, P, dS = P (dP - D), then dV^T += dO^T P and
+//     dK^T += Q^T dS.  Q, dO, lse and D go straight to LDS in a ring of
+//     three chunks, last chunk first; dO^T and Q^T come from transpose
+//     loads.  (bwd_kv: the same as two passes, dV then dK, each with one
+//     accumulator tile; a test hook.)
+//   * bwd_reduce: with grouped K/V heads the key-side kernel writes one
+//     fp32 dk, dv per query head into the workspace and this kernel sums
+//     each group in head order into the bf16 outputs.
 // Causal tiles entirely outside the triangle are never visited; the heaviest
 // tiles are dispatched first.
+
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -285,15 +288,17 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
 // ------------------------------------------------------------- dk and dv --
 
-// One pass per gradient (MODE = kDV or kDK): a wave owns 32 keys, whose K
-// (and for dK, V) rows stay in registers as B operands; query chunks of 32
-// are staged in LDS.  Splitting dV from dK recomputes S once more but keeps
-// each pass within two waves per SIMD (a fused pass would hold both 32-key
-// accumulator tiles, K and V, and spill).
-//   dV pass: S = Q K^T, P = 2^(c s - lse2), dV^T += dO^T P
-//   dK pass: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
-// Q and dO are staged row-major; dO^T and Q^T come from transpose loads.
-constexpr int kDV = 0, kDK = 1;
+// The key side: a wave owns 32 keys, whose K (and V) rows stay in
+// registers as B operands; query chunks of 32 are staged in LDS.
+//   fused (MODE = kDKV): S = Q K^T, dP = dO V^T, P = 2^(c s - lse2),
+//     dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS
+//   dV pass (kDV): S, P, dV^T += dO^T P
+//   dK pass (kDK): S, dP, dS, dK^T += Q^T dS
+// The fused pass computes S once instead of twice, but holds both 32-key
+// accumulator tiles.  The passes take the same steps in the same order, so
+// the results are the same bits either way.  Q and dO are staged row-major;
+// dO^T and Q^T come from transpose loads.
+constexpr int kDV = 0, kDK = 1, kDKV = 2;
 constexpr int kKvRun = 4;           // key tiles of one head kept on one XCD
 
 template <int D>
@@ -307,12 +312,13 @@ struct KvStage {
 };
 
 template <int D, bool CAUSAL, int MODE>
-__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-              const float* __restrict__ lse, const float* __restrict__ delta,
-              uint16_t* __restrict__ out, float* __restrict__ out32, int Hq, int Hkv, int N, int BH,
-              float c, float scale) {
+__device__ __forceinline__ void bwd_kv_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                                            const float* __restrict__ lse, const float* __restrict__ delta,
+                                            uint16_t* __restrict__ out, float* __restrict__ out32,
+                                            uint16_t* __restrict__ outv, float* __restrict__ outv32, int Hq,
+                                            int Hkv, int N, int BH, float c, float scale) {
+    constexpr bool KV = MODE == kDKV;     // both gradients in one pass
     using L = BwTile<D>;
     using St = KvStage<D>;
     // the ring of chunks: separate LDS arrays, the loop unrolled by three (see
@@ -350,12 +356,12 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const bool wave_active = wkey0 < N;
 
     // This lane's key row of K (and V) as B operands (dims 16*ks + 8*hi .. +7).
-    bf16x8 kf[D / 16], vf[MODE == kDK ? D / 16 : 1];
+    bf16x8 kf[D / 16], vf[MODE != kDV ? D / 16 : 1];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = (uint32_t)(mykey * D + ks * 16 + hi * 8) * 2;
         kf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(krs, off));
-        if constexpr (MODE == kDK) vf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(vrs, off));
+        if constexpr (MODE != kDV) vf[ks] = __builtin_bit_cast(bf16x8, buf_ld16(vrs, off));
     }
 
     // Query chunks: all, or (causal) those with a query >= key0.
@@ -371,7 +377,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int i = 0; i < L::INST; ++i) soff[i] = bw_src_offset<D>(i, wave, lane);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
-    constexpr int OPS = 2 * L::INST + 1 + (MODE == kDK ? 1 : 0);   // vector memory ops per chunk
+    constexpr int OPS = 2 * L::INST + 1 + (MODE != kDV ? 1 : 0);   // vector memory ops per chunk
 
     auto issue_loads = [&](int cj, uint16_t* base) {
         const uint32_t t0 = (uint32_t)cj * BW_T * D * 2;
@@ -382,14 +388,19 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         const uint32_t so = (uint32_t)(cj * BW_T + lane) * 4;
         buf_ld4_lds(lrs, base + St::STATS, so);
-        if constexpr (MODE == kDK) buf_ld4_lds(drs, base + St::STATS + 128, so);
+        if constexpr (MODE != kDV) buf_ld4_lds(drs, base + St::STATS + 128, so);
     };
 
-    f32x16 acc[D / 32];
+    f32x16 acc[D / 32], accv[KV ? D / 32 : 1];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    if constexpr (KV)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accv[db][r] = 0.f;
 
     const int nq = n_c - c_first;                    // >= 1 (key0 < N)
     // Chunks are taken from the last one back to c_first: the workgroups of
@@ -427,7 +438,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             auto rd = [&](int ks) {
                 const int e = bw_rm<D>(l32, ks * 2 + hi);
                 qa[ks] = *reinterpret_cast<const bf16x8*>(base + St::QRM + e);
-                if constexpr (MODE == kDK) ga[ks] = *reinterpret_cast<const bf16x8*>(base + St::GRM + e);
+                if constexpr (MODE != kDV) ga[ks] = *reinterpret_cast<const bf16x8*>(base + St::GRM + e);
             };
 #pragma unroll
             for (int ks = 0; ks < KPF; ++ks) rd(ks);
@@ -436,7 +447,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 if (ks + KPF < D / 16) rd(ks + KPF);
                 __builtin_amdgcn_sched_barrier(0);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sacc, 0, 0, 0);
-                if constexpr (MODE == kDK)
+                if constexpr (MODE != kDV)
                     pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], pacc, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -450,7 +461,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 for (int rg = 0; rg < 4; ++rg) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 8 * rg + 4 * hi);
                     f32x4 d4;
-                    if constexpr (MODE == kDK) d4 = *reinterpret_cast<const f32x4*>(stats + 64 + 8 * rg + 4 * hi);
+                    if constexpr (MODE != kDV) d4 = *reinterpret_cast<const f32x4*>(stats + 64 + 8 * rg + 4 * hi);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rg * 4 + i;
@@ -461,6 +472,7 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             p = ok ? p : 0.f;
                         }
                         if constexpr (MODE == kDK) p *= pacc[r] - d4[i];
+                        if constexpr (KV) pacc[r] = p * (pacc[r] - d4[i]);   // dS beside P
                         sacc[r] = p;
                     }
                 }
@@ -471,16 +483,36 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 weights(std::false_type{});
             // dV^T += dO^T P, or dK^T += Q^T dS: 16 queries per MFMA, the
             // transposed operand by transpose loads from the row-major tile.
-            const uint16_t* At = base + (MODE == kDV ? St::GRM : St::QRM);
+            if constexpr (KV) {
+                // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-            for (int c16 = 0; c16 < BW_T / 16; ++c16) {
-                bf16x8 pb;
+                for (int c16 = 0; c16 < BW_T / 16; ++c16) {
+                    bf16x8 pp, pd;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[c16 * 8 + i];
+                    for (int i = 0; i < 8; ++i) {
+                        pp[i] = (__bf16)sacc[c16 * 8 + i];
+                        pd[i] = (__bf16)pacc[c16 * 8 + i];
+                    }
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 a = bw_tr_operand<D>(At, lane, db, c16);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x8 ag = bw_tr_operand<D>(base + St::GRM, lane, db, c16);
+                        accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pp, accv[db], 0, 0, 0);
+                        const bf16x8 aq = bw_tr_operand<D>(base + St::QRM, lane, db, c16);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pd, acc[db], 0, 0, 0);
+                    }
+                }
+            } else {
+                const uint16_t* At = base + (MODE == kDV ? St::GRM : St::QRM);
+#pragma unroll
+                for (int c16 = 0; c16 < BW_T / 16; ++c16) {
+                    bf16x8 pb;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[c16 * 8 + i];
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x8 a = bw_tr_operand<D>(At, lane, db, c16);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -493,31 +525,59 @@ bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     if (mykey < N) {
         // lane = key row; entry r of block db = dim 32db + 8(r/4) + 4hi + r%4
-        const float f = MODE == kDK ? scale : 1.f;
-        if (out32 == nullptr) {
-            uint16_t* row = out + (((size_t)b * Hkv + g) * N + mykey) * D;
+        auto store = [&](const f32x16 (&a)[D / 32], float f, uint16_t* o16, float* o32) {
+            if (o32 == nullptr) {
+                uint16_t* row = o16 + (((size_t)b * Hkv + g) * N + mykey) * D;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int dim0 = db * 32 + rg * 8 + hi * 4;
-                    *reinterpret_cast<u32x2*>(row + dim0) =
-                        u32x2{pack_bf16x2(acc[db][rg * 4] * f, acc[db][rg * 4 + 1] * f),
-                              pack_bf16x2(acc[db][rg * 4 + 2] * f, acc[db][rg * 4 + 3] * f)};
-                }
-        } else {
-            float* row = out32 + ((size_t)bh * N + mykey) * D;
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dim0 = db * 32 + rg * 8 + hi * 4;
+                        *reinterpret_cast<u32x2*>(row + dim0) =
+                            u32x2{pack_bf16x2(a[db][rg * 4] * f, a[db][rg * 4 + 1] * f),
+                                  pack_bf16x2(a[db][rg * 4 + 2] * f, a[db][rg * 4 + 3] * f)};
+                    }
+            } else {
+                float* row = o32 + ((size_t)bh * N + mykey) * D;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int dim0 = db * 32 + rg * 8 + hi * 4;
-                    *reinterpret_cast<f32x4*>(row + dim0) =
-                        f32x4{acc[db][rg * 4] * f, acc[db][rg * 4 + 1] * f, acc[db][rg * 4 + 2] * f,
-                              acc[db][rg * 4 + 3] * f};
-                }
-        }
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dim0 = db * 32 + rg * 8 + hi * 4;
+                        *reinterpret_cast<f32x4*>(row + dim0) =
+                            f32x4{a[db][rg * 4] * f, a[db][rg * 4 + 1] * f, a[db][rg * 4 + 2] * f,
+                                  a[db][rg * 4 + 3] * f};
+                    }
+            }
+        };
+        store(acc, MODE == kDV ? 1.f : scale, out, out32);
+        if constexpr (KV) store(accv, 1.f, outv, outv32);
     }
+}
+
+// The two passes at two waves per SIMD.  The fused pass holds both
+// accumulator tiles: at d = 64 that still fits two waves per SIMD; at
+// d = 128 it takes one wave per SIMD, with up to 512 registers (the
+// accumulators in AGPRs), which beats the two passes' extra S products.
+template <int D, bool CAUSAL, int MODE>
+__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+              const float* __restrict__ lse, const float* __restrict__ delta,
+              uint16_t* __restrict__ out, float* __restrict__ out32, int Hq, int Hkv, int N, int BH,
+              float c, float scale) {
+    bwd_kv_body<D, CAUSAL, MODE>(q, k, v, dout, lse, delta, out, out32, nullptr, nullptr, Hq, Hkv, N, BH, c,
+                                 scale);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(BW_THREADS) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+bwd_kvf_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+               const float* __restrict__ lse, const float* __restrict__ delta,
+               uint16_t* __restrict__ dk, float* __restrict__ dk32, uint16_t* __restrict__ dv,
+               float* __restrict__ dv32, int Hq, int Hkv, int N, int BH, float c, float scale) {
+    bwd_kv_body<D, CAUSAL, kDKV>(q, k, v, dout, lse, delta, dk, dk32, dv, dv32, Hq, Hkv, N, BH, c, scale);
 }
 
 // ---------------------------------------------------------------- reduce --
@@ -573,16 +633,27 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     const long long kv_units = (long long)((n_qt + kKvRun - 1) / kKvRun) * kKvRun * BH;
     const long long kv_round = (long long)kXcds * kKvRun;
     const unsigned kv_grid = (unsigned)((kv_units + kv_round - 1) / kv_round * kv_round);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDV>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
-                       delta, static_cast<uint16_t*>(a.dv), dv32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDK>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
-                       delta, static_cast<uint16_t*>(a.dk), dk32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
+    // Both key-side gradients in one pass; ATTN_BWD_TWO_PASS=1 (a test
+    // hook) runs the dV and dK passes instead, which give the same bits.
+    const char* two = getenv("ATTN_BWD_TWO_PASS");
+    if (!(two != nullptr && two[0] == '1' && two[1] == '\0')) {
+        hipLaunchKernelGGL((bwd_kvf_kernel<D, CAUSAL>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                           delta, static_cast<uint16_t*>(a.dk), dk32, static_cast<uint16_t*>(a.dv), dv32, a.Hq,
+                           a.Hkv, a.N, BH, c, a.scale);
+    } else {
+        hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDV>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                           delta, static_cast<uint16_t*>(a.dv), dv32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, kDK>), dim3(kv_grid), dim3(BW_THREADS), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
+                           delta, static_cast<uint16_t*>(a.dk), dk32, a.Hq, a.Hkv, a.N, BH, c, a.scale);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || G == 1) return e;
 

@@ -2,8 +2,9 @@
 of dq, dk and dv on ragged shapes (one row, tile edges, several tiles and a
 ragged tail), causal and not, grouped and ungrouped heads, d = 64 and 128,
 scales 0, negative and default, and the full causal GQA 8192-token workload;
-plus determinism, the scale-0 closed form on the GPU, and the autograd
-wrapper that joins attn_fwd and attn_bwd.
+plus determinism, the scale-0 closed form on the GPU, the fused key-side
+pass against the two-pass one, and the autograd wrapper that joins
+attn_fwd and attn_bwd.
 
 Tolerance (derived in the design notes): every gradient element within
 2e-2 * max(1, max |reference| of that tensor) - the bf16 output rounding is
@@ -133,3 +134,19 @@ def test_autograd_attention(causal):
     ref = OB.attention_bwd(f64(q), f64(k), f64(v), f64(do), 1.0 / math.sqrt(d), causal)
     for g, r in zip((qd.grad, kd.grad, vd.grad), ref):
         assert np.abs(f64(g.cpu()) - r).max() <= REL * max(1.0, float(np.abs(r).max()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2)])
+def test_fused_key_side_matches_two_passes(monkeypatch, d, causal, Hq, Hkv):
+    """The key-side gradients in one pass (the default) and in two passes
+    (dV, then dK; ATTN_BWD_TWO_PASS=1) take the same steps in the same
+    order: dq, dk and dv agree bit for bit."""
+    q, k, v = dense_inputs(B=1, Hq=Hq, Hkv=Hkv, N=333, d=d, dtype="bf16", seed=15 + d)
+    do = _dout((1, Hq, 333, d), 16 + d)
+    a = run(q, k, v, do, 1.0 / math.sqrt(d), causal)
+    monkeypatch.setenv("ATTN_BWD_TWO_PASS", "1")
+    b = run(q, k, v, do, 1.0 / math.sqrt(d), causal)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
