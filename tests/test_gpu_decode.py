@@ -277,15 +277,17 @@ def test_bad_device_inputs_give_nan(monkeypatch, waves, Hq, Hkv):
         assert max_abs(lse[s].double().numpy(), ref_l[s]) <= LSE_TOL
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("Hq", [12, 64])
+def test_graph_replay_matches_eager(Hq):
     """The decode step captured in a HIP graph: replayed several times, with
     eager library calls in between and the inputs rewritten in place between
     replays (new queries, one more token per sequence written into its block),
-    every replay equals an eager call on the same buffers bit for bit."""
+    every replay equals an eager call on the same buffers bit for bit (also
+    with 32 query heads per kv head, read by teams of two waves)."""
     from exact_tiled_self_amd.graph import DecodeGraph
     rng = np.random.default_rng(71)
     ctx = rng.integers(100, 3000, 16)
-    p = paged_inputs(small_cfg(), S=16, ctx_lens=ctx.tolist(), extra_blocks=40, max_blocks=200, seed=72)
+    p = paged_inputs(small_cfg(Hq, 2), S=16, ctx_lens=ctx.tolist(), extra_blocks=40, max_blocks=200, seed=72)
     d = _dev(p)
     # free pool blocks (never referenced) to grow into
     used = set(p["block_table"].numpy()[p["block_table"].numpy() >= 0].tolist())
