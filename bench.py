@@ -202,6 +202,21 @@ def dense_kernel_name(cfg) -> str:
             f"{32 if cfg.d == 64 else 64}-key tiles>")
 
 
+# The committed rocprofv3 summary of each dense workload (profiles/<name>.md)
+# and the sources its digest covers.
+DENSE_PROFILES = {
+    "vit_b16_fp32": ("prefill_f32_d64_vit_b16_b1_n196", ["prefill_f32.hip", "common.h", "internal.h"]),
+    "vit_b16_bf16": ("prefill_bf16_d64_vit_b16_b64_n196",
+                     ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"]),
+    "vit_b16_bf16_n577": ("prefill_bf16_d64_vit_b16_b64_n577",
+                          ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"]),
+    "gqa_causal_t8192": ("prefill_bf16_d128_causal_gqa_t8192",
+                         ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"]),
+    "mha_causal_t32768": ("prefill_bf16_d128_causal_mha_t32768",
+                          ["prefill_bf16.hip", "prefill_tile.h", "common.h", "internal.h"]),
+}
+
+
 def time_dense(torch, dev, stream, cfg, steps, warmup):
     """attn_fwd alone on one dense workload, inputs resident: HIP events on
     the launch stream around every call.  Returns the timing record."""
@@ -242,7 +257,10 @@ def time_dense(torch, dev, stream, cfg, steps, warmup):
         "GB/s": round(gb, 1), "frac_hbm": round(gb / PEAK_HBM_GBPS, 4),
         "roof_TFLOP/s": round(roof, 1), "roof_bound": "mfma" if roof == peak else "hbm",
         "frac_roof": round(tf / roof, 4),
-        "flops": fl, "algorithmic_bytes": int(by), "kernel": dense_kernel_name(cfg)}
+        "flops": fl, "algorithmic_bytes": int(by), "kernel": dense_kernel_name(cfg),
+        # HBM bytes per launch counted by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+        # calibrated) in the committed profile; null if its sources changed
+        "traffic": (profiled_traffic(*DENSE_PROFILES[cfg.name]) if cfg.name in DENSE_PROFILES else None)}
 
 
 def run_configs(names, steps, warmup, copy_mib=0):
