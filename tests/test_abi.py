@@ -379,3 +379,14 @@ def test_binding_rejects_wrong_fusion_outputs():
     _expect_bad_output(lambda: _lib.attn_swiglu(gu, out=torch.zeros(4, 512, dtype=torch.bfloat16)),
                        "out must have shape")
     _expect_bad_output(lambda: _lib.attn_swiglu(x, x, out=torch.zeros(4, 256)), "out must have dtype")
+
+
+def test_autograd_wrapper_has_no_cpu_path():
+    """attention() (the autograd function over attn_fwd and attn_bwd) passes
+    host tensors to the binding, which refuses them: there is no CPU
+    fallback."""
+    from exact_tiled_self_amd import attention
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, requires_grad=True)
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="device"):
+        attention(q, k, k, causal=True)
